@@ -1,0 +1,60 @@
+"""The oracle's pins must catch plausible mistakes: each case below plants one error in a
+copy of the oracle source (on the CPU only), builds it, and runs the pin suite against it; the
+suite must fail.  The unmodified source must pass (checked by the pin suite itself)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "adamw4_oracle.c")
+
+MUTANTS = {
+    "no_bias_correction_v": ("s.rs2 = (float)(1.0 / sqrt(bc2));", "s.rs2 = 1.0f;"),
+    "no_bias_correction_m": ("s.step_size = (float)((double)hp->lr / bc1);",
+                             "s.step_size = hp->lr;"),
+    "decay_sign": ("s.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);",
+                   "s.decay = (float)(1.0 + (double)hp->lr * (double)hp->weight_decay);"),
+    "v_uses_g_not_g2": ("float gg = g * g;", "float gg = g;"),
+    "m_beta_swapped": ("float m1 = hp->beta1 * m;", "float m1 = s->omb1 * m;"),
+    "eps_dropped": ("den = den + hp->eps;", "den = den + 0.0f;"),
+    "weights_after_quant": ("orc_elem r = adamw_elem(w[i], widen_grad(g, g_bf16, i), m, v, hp, &s);\n                w[i] = r.w;",
+                            "orc_elem r = adamw_elem(w[i], widen_grad(g, g_bf16, i), m, v, hp, &s);\n                w[i] = r.w + 0.5f * (r.m - m) * s.step_size;"),
+    "zip_sqrt_swapped": ("float n2 = sb + sa;", "float n2 = sb + sy;"),
+    "zip_choice_inverted": ("codes[j] = (uint8_t)(u < p ? k : k + 1);\n    }\n}\n\n/* v block under ZE-EDEN",
+                            "codes[j] = (uint8_t)(u < p ? k + 1 : k);\n    }\n}\n\n/* v block under ZE-EDEN"),
+    "zip_state_space_p": ("float p = orc_zip_p(y, lo, hi, c, eps);", "float p = (hi - y) / (hi - lo);"),
+    "m_sr_p_inverted": ("float p = (hi - y) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 1, i0 + j);",
+                        "float p = (y - lo) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 1, i0 + j);"),
+    "rtn_ties_high": ("if (y > mid) ++code;", "if (y >= mid) ++code;"),
+    "nibble_order": ("bytes[q] = (uint8_t)(lo | (hi << 4));", "bytes[q] = (uint8_t)(hi | (lo << 4));"),
+    "eden_gamma_inverted": ("float gamma = nrm / fmaxf(dot, 1e-12f);", "float gamma = dot / fmaxf(nrm, 1e-12f);"),
+    "eden_no_rescale": ("*scale = gamma * s;", "*scale = s;"),
+    "philox_key_bump": ("k1 += 0xBB67AE85u;", "k1 += 0x9E3779B9u;"),
+    "rng_stream_ignored": ("(uint32_t)(j >> 32) | ((uint32_t)stream << 31)", "(uint32_t)(j >> 32)"),
+    "prev_mode_ignored": ("const float* Vin = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZIP_SR) ? V0 : V1;",
+                          "const float* Vin = (hp->mode == ORC_ZIP_SR) ? V0 : V1;"),
+    "v0_codebook_k16": ("out[k] = (float)((double)k / 15.0);", "out[k] = (float)((double)k / 16.0);"),
+    "nf4_delta": ("const double delta = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);",
+                  "const double delta = 0.9677083;"),
+    "absmax_not_abs": ("for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, fabsf(x[j]));",
+                       "for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    "-o", str(lib), str(mut), "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, ADAMW4_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode != 0, f"pin suite passed with mutant {name}:\n{r.stdout[-2000:]}"
