@@ -1,0 +1,45 @@
+"""Build the HIP library libadamw4.so in-tree for gfx950.
+
+Flags: -ffp-contract=off keeps one rounding per FP32 operation in the code paths that decide
+stored bits (clang-HIP's defaults already give correctly rounded division and square root and
+keep FP32 denormals); packed-FP32 instructions are disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libadamw4.so")
+SOURCES = [os.path.join(CSRC, "adamw4_kernels.hip"), os.path.join(CSRC, "adamw4_api.cpp")]
+ARCH = os.environ.get("ADAMW4_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def flags() -> list[str]:
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libadamw4.so (always recompiles)."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc()] + flags() + ["-shared", "-o", tmp] + SOURCES
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    if verbose and (r.stdout or r.stderr):
+        print(r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

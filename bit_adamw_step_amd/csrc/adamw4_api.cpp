@@ -1,0 +1,381 @@
+// adamw4_api.cpp -- host runtime behind the C ABI in include/adamw4.h: argument checks,
+// per-step scalars, the multi-tensor work plan (descriptor + chunk tables in device memory,
+// cached across steps), and the launches.
+//
+// Per-step scalars follow the AdamW of the pages (bias-corrected moments inside
+// h(v) = 1/(sqrt(v/(1-beta2^t)) + eps) on daiwk.github.io "ZIP-SR / ZE-EDEN: 4-bit AdamW state
+// quantization", section "Core equation"; decoupled weight decay as on the kongchang.com
+// explainer): bc1 = 1 - beta1^t and bc2 = 1 - beta2^t in binary64, then
+// step_size = lr/bc1, rs2 = 1/sqrt(bc2), decay = 1 - lr*wd each rounded once to FP32.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/adamw4.h"
+#include "adamw4_internal.h"
+
+using namespace adamw4;
+
+namespace {
+
+constexpr size_t kNoOffset = SIZE_MAX;
+constexpr int kMaxPlans = 8;
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+bool quantized(int64_t n, uint32_t flags) { return n >= kMinQuant && !(flags & ADAMW4_T_NORM); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Section offsets and total size of one tensor's state.
+size_t layout(int64_t n, uint32_t flags, size_t off[4]) {
+    if (quantized(n, flags)) {
+        const size_t codes = align16(size_t((n + 1) / 2));
+        const size_t scales = align16(size_t((n + kBlock - 1) / kBlock) * 4);
+        off[0] = 0;
+        off[1] = codes;
+        off[2] = 2 * codes;
+        off[3] = 2 * codes + scales;
+        return 2 * codes + 2 * scales;
+    }
+    const size_t mv = align16(size_t(n) * 4);
+    off[0] = 0;
+    off[1] = mv;
+    off[2] = kNoOffset;
+    off[3] = kNoOffset;
+    return 2 * mv;
+}
+
+adamw4_status check_tensor_common(const adamw4_tensor& t) {
+    if (t.numel < 1) return ADAMW4_EINVAL;
+    if (t.numel > ADAMW4_MAX_NUMEL) return ADAMW4_ESIZE;
+    if (t.flags & ~uint32_t(ADAMW4_T_NORM | ADAMW4_T_HEAD)) return ADAMW4_EINVAL;
+    if (!t.state) return ADAMW4_EINVAL;
+    if (!aligned16(t.state)) return ADAMW4_EALIGN;
+    size_t off[4];
+    if (t.state_size < layout(t.numel, t.flags, off)) return ADAMW4_ESIZE;
+    return ADAMW4_OK;
+}
+
+adamw4_status check_tensor_step(const adamw4_tensor& t) {
+    adamw4_status s = check_tensor_common(t);
+    if (s != ADAMW4_OK) return s;
+    if (!t.param || !t.grad) return ADAMW4_EINVAL;
+    if (t.grad_dtype != ADAMW4_GRAD_F32 && t.grad_dtype != ADAMW4_GRAD_BF16) return ADAMW4_EINVAL;
+    if (!aligned16(t.param) || !aligned16(t.grad)) return ADAMW4_EALIGN;
+    return ADAMW4_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+adamw4_status check_hparams(const adamw4_hparams& h) {
+    if (h.step < 1 || h.step > int64_t(UINT32_MAX)) return ADAMW4_EINVAL;
+    if (!(h.beta1 >= 0.0f && h.beta1 < 1.0f)) return ADAMW4_EINVAL;
+    if (!(h.beta2 >= 0.0f && h.beta2 < 1.0f)) return ADAMW4_EINVAL;
+    if (!(h.eps > 0.0f) || !finite(h.eps)) return ADAMW4_EINVAL;
+    if (!finite(h.lr) || !finite(h.weight_decay)) return ADAMW4_EINVAL;
+    if (h.mode != ADAMW4_ZIP_SR && h.mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
+    if (h.prev_mode != -1 && h.prev_mode != ADAMW4_ZIP_SR && h.prev_mode != ADAMW4_ZE_EDEN)
+        return ADAMW4_EINVAL;
+    if (h.sr_head != 0 && h.sr_head != 1) return ADAMW4_EINVAL;
+    return ADAMW4_OK;
+}
+
+StepArgs step_args(const adamw4_hparams& h) {
+    const double b1 = h.beta1, b2 = h.beta2, t = double(h.step);
+    const double bc1 = 1.0 - std::pow(b1, t);
+    const double bc2 = 1.0 - std::pow(b2, t);
+    StepArgs a;
+    a.step_size = float(double(h.lr) / bc1);
+    a.rs2 = float(1.0 / std::sqrt(bc2));
+    a.decay = float(1.0 - double(h.lr) * double(h.weight_decay));
+    a.omb1 = float(1.0 - b1);
+    a.omb2 = float(1.0 - b2);
+    a.beta1 = h.beta1;
+    a.beta2 = h.beta2;
+    a.eps = h.eps;
+    a.seed_lo = uint32_t(h.seed);
+    a.seed_hi = uint32_t(h.seed >> 32);
+    a.t = uint32_t(h.step);
+    a.mode = h.mode;
+    a.vin_mode = (h.prev_mode < 0) ? h.mode : h.prev_mode;
+    a.sr_head = h.sr_head;
+    return a;
+}
+
+TensorDesc make_desc(const adamw4_tensor& t, uint32_t pos) {
+    TensorDesc d;
+    std::memset(&d, 0, sizeof(d));
+    size_t off[4];
+    layout(t.numel, t.flags, off);
+    char* base = static_cast<char*>(t.state);
+    d.param = t.param;
+    d.grad = t.grad;
+    d.numel = t.numel;
+    d.pos = pos;
+    d.flags = 0;
+    if (quantized(t.numel, t.flags)) d.flags |= D_QUANT;
+    if (t.flags & ADAMW4_T_HEAD) d.flags |= D_HEAD;
+    if (t.grad_dtype == ADAMW4_GRAD_BF16) d.flags |= D_BF16;
+    d.s0 = base + off[0];
+    d.s1 = base + off[1];
+    if (d.flags & D_QUANT) {
+        d.s2 = reinterpret_cast<float*>(base + off[2]);
+        d.s3 = reinterpret_cast<float*>(base + off[3]);
+    }
+    return d;
+}
+
+// Device memory for one launch's descriptors and chunk table.
+struct Plan {
+    int device = -1;
+    std::vector<TensorDesc> descs;  // host copy, also the cache key
+    uint32_t nchunks = 0;
+    uint32_t chunk_units = 0;
+    void* dbuf = nullptr;
+    uint64_t last_use = 0;
+};
+
+struct DeviceInfo {
+    int cus = 0;
+    int step_bpc = 0;
+    int aux_bpc = 0;
+};
+
+std::mutex g_mu;
+std::vector<Plan*> g_plans;
+uint64_t g_clock = 0;
+std::vector<DeviceInfo> g_dev;
+
+adamw4_status device_info(int dev, DeviceInfo& out) {
+    if (dev < 0) return ADAMW4_EHIP;
+    if (size_t(dev) >= g_dev.size()) g_dev.resize(dev + 1);
+    DeviceInfo& di = g_dev[dev];
+    if (di.cus == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return ADAMW4_EHIP;
+        di.cus = std::max(cus, 1);
+        di.step_bpc = step_blocks_per_cu();
+        di.aux_bpc = aux_blocks_per_cu();
+    }
+    out = di;
+    return ADAMW4_OK;
+}
+
+// Chunk size: 64 units (8192 values) for large lists; smaller when the list is too small to
+// give every CU several chunks, but never below one workgroup iteration (16 units).
+uint32_t pick_chunk_units(uint64_t total_units, int cus) {
+    uint64_t target = total_units / (uint64_t(cus) * 8);
+    uint32_t cu = 64;
+    while (cu > uint32_t(kRows) && cu > target) cu >>= 1;
+    return cu;
+}
+
+// Build descriptor and chunk tables and copy them to a fresh device buffer.
+adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan*& out) {
+    uint64_t total_units = 0;
+    for (const TensorDesc& d : descs) total_units += uint64_t((d.numel + kBlock - 1) / kBlock);
+    const uint32_t cu = pick_chunk_units(total_units, cus);
+    std::vector<Chunk> chunks;
+    uint64_t nch = 0;
+    for (const TensorDesc& d : descs) nch += (uint64_t((d.numel + kBlock - 1) / kBlock) + cu - 1) / cu;
+    if (nch > UINT32_MAX) return ADAMW4_ESIZE;
+    chunks.reserve(size_t(nch));
+    for (size_t i = 0; i < descs.size(); ++i) {
+        const uint64_t units = uint64_t((descs[i].numel + kBlock - 1) / kBlock);
+        for (uint64_t u = 0; u < units; u += cu) chunks.push_back(Chunk{uint32_t(i), uint32_t(u)});
+    }
+    const size_t dbytes = align16(descs.size() * sizeof(TensorDesc));
+    const size_t bytes = dbytes + chunks.size() * sizeof(Chunk);
+    void* dbuf = nullptr;
+    if (hipMalloc(&dbuf, std::max<size_t>(bytes, 16)) != hipSuccess) return ADAMW4_ENOMEM;
+    std::vector<char> host(bytes);
+    std::memcpy(host.data(), descs.data(), descs.size() * sizeof(TensorDesc));
+    std::memcpy(host.data() + dbytes, chunks.data(), chunks.size() * sizeof(Chunk));
+    // a fresh buffer: a blocking copy orders it before any later use on any stream
+    if (hipMemcpy(dbuf, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dbuf);
+        return ADAMW4_EHIP;
+    }
+    Plan* p = new Plan;
+    p->device = dev;
+    p->descs = std::move(descs);
+    p->nchunks = uint32_t(chunks.size());
+    p->chunk_units = cu;
+    p->dbuf = dbuf;
+    out = p;
+    return ADAMW4_OK;
+}
+
+void free_plan(Plan* p) {
+    if (p->dbuf) (void)hipFree(p->dbuf);
+    delete p;
+}
+
+Launch launch_of(const Plan& p, int grid_cap) {
+    Launch L;
+    L.descs = static_cast<const TensorDesc*>(p.dbuf);
+    L.chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(p.dbuf) +
+                                              align16(p.descs.size() * sizeof(TensorDesc)));
+    L.nchunks = p.nchunks;
+    L.chunk_units = p.chunk_units;
+    L.grid = int(std::min<uint64_t>(p.nchunks, uint64_t(std::max(grid_cap, 1))));
+    return L;
+}
+
+// Find or create the cached plan for this descriptor list (the common case in training: the
+// same buffers every step, so the tables are uploaded once).  Evicting a plan waits for the
+// device so no in-flight launch still reads it.
+adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan*& out) {
+    for (Plan* p : g_plans) {
+        if (p->device == dev && p->descs.size() == descs.size() &&
+            std::memcmp(p->descs.data(), descs.data(), descs.size() * sizeof(TensorDesc)) == 0) {
+            p->last_use = ++g_clock;
+            out = p;
+            return ADAMW4_OK;
+        }
+    }
+    Plan* p = nullptr;
+    adamw4_status s = build_plan(std::move(descs), dev, cus, p);
+    if (s != ADAMW4_OK) return s;
+    if (g_plans.size() >= size_t(kMaxPlans)) {
+        auto lru = std::min_element(g_plans.begin(), g_plans.end(),
+                                    [](const Plan* a, const Plan* b) { return a->last_use < b->last_use; });
+        (void)hipDeviceSynchronize();
+        free_plan(*lru);
+        g_plans.erase(lru);
+    }
+    p->last_use = ++g_clock;
+    g_plans.push_back(p);
+    out = p;
+    return ADAMW4_OK;
+}
+
+adamw4_status current_device(int& dev) {
+    if (hipGetDevice(&dev) != hipSuccess) return ADAMW4_EHIP;
+    return ADAMW4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t adamw4_state_bytes(int64_t numel, uint32_t flags) {
+    if (numel < 1 || numel > ADAMW4_MAX_NUMEL) return 0;
+    size_t off[4];
+    return layout(numel, flags, off);
+}
+
+adamw4_status adamw4_state_layout(int64_t numel, uint32_t flags, size_t offsets[4]) {
+    if (!offsets || numel < 1 || numel > ADAMW4_MAX_NUMEL) return ADAMW4_EINVAL;
+    layout(numel, flags, offsets);
+    return ADAMW4_OK;
+}
+
+adamw4_status adamw4_codebook(int32_t which, float out[16]) {
+    if (!out || which < 0 || which > 2) return ADAMW4_EINVAL;
+    codebook_words(which, out);
+    return ADAMW4_OK;
+}
+
+adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
+                          void* stream) {
+    if (!hp || n < 0 || (n > 0 && !ts)) return ADAMW4_EINVAL;
+    if (n > ADAMW4_MAX_TENSORS) return ADAMW4_ESIZE;
+    adamw4_status s = check_hparams(*hp);
+    if (s != ADAMW4_OK) return s;
+    for (int32_t i = 0; i < n; ++i)
+        if ((s = check_tensor_step(ts[i])) != ADAMW4_OK) return s;
+    if (n == 0) return ADAMW4_OK;
+
+    std::vector<TensorDesc> descs(static_cast<size_t>(n));
+    for (int32_t i = 0; i < n; ++i) descs[i] = make_desc(ts[i], uint32_t(i));
+    const StepArgs a = step_args(*hp);
+
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if ((s = current_device(dev)) != ADAMW4_OK) return s;
+    DeviceInfo di;
+    if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
+    Plan* p = nullptr;
+    if ((s = get_plan(std::move(descs), dev, di.cus, p)) != ADAMW4_OK) return s;
+    const Launch L = launch_of(*p, di.cus * di.step_bpc);
+    if (launch_step(L, a, static_cast<hipStream_t>(stream)) != hipSuccess) return ADAMW4_EHIP;
+    return ADAMW4_OK;
+}
+
+// init and decode: a one-off plan, freed after the stream has finished with it.
+static adamw4_status run_aux(std::vector<TensorDesc>&& descs, bool init, int32_t mode,
+                             void* stream) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    adamw4_status s;
+    if ((s = current_device(dev)) != ADAMW4_OK) return s;
+    DeviceInfo di;
+    if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
+    Plan* p = nullptr;
+    if ((s = build_plan(std::move(descs), dev, di.cus, p)) != ADAMW4_OK) return s;
+    const Launch L = launch_of(*p, di.cus * di.aux_bpc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = init ? launch_init(L, mode, st) : launch_decode(L, mode, st);
+    hipError_t e2 = hipStreamSynchronize(st);
+    free_plan(p);
+    return (e == hipSuccess && e2 == hipSuccess) ? ADAMW4_OK : ADAMW4_EHIP;
+}
+
+adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode,
+                                const float* const* m0, const float* const* v0, void* stream) {
+    if (n < 0 || (n > 0 && !ts)) return ADAMW4_EINVAL;
+    if (n > ADAMW4_MAX_TENSORS) return ADAMW4_ESIZE;
+    if (mode != ADAMW4_ZIP_SR && mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
+    adamw4_status s;
+    for (int32_t i = 0; i < n; ++i) {
+        if ((s = check_tensor_common(ts[i])) != ADAMW4_OK) return s;
+        const float* a = m0 ? m0[i] : nullptr;
+        const float* b = v0 ? v0[i] : nullptr;
+        if ((a && !aligned16(a)) || (b && !aligned16(b))) return ADAMW4_EALIGN;
+    }
+    if (n == 0) return ADAMW4_OK;
+    std::vector<TensorDesc> descs(static_cast<size_t>(n));
+    for (int32_t i = 0; i < n; ++i) {
+        adamw4_tensor t = ts[i];
+        descs[i] = make_desc(t, uint32_t(i));
+        descs[i].aux0 = const_cast<float*>(m0 ? m0[i] : nullptr);
+        descs[i].aux1 = const_cast<float*>(v0 ? v0[i] : nullptr);
+    }
+    return run_aux(std::move(descs), true, mode, stream);
+}
+
+adamw4_status adamw4_decode_state(const adamw4_tensor* t, int32_t mode, float* m_out,
+                                  float* v_out, void* stream) {
+    if (!t) return ADAMW4_EINVAL;
+    if (mode != ADAMW4_ZIP_SR && mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
+    adamw4_status s = check_tensor_common(*t);
+    if (s != ADAMW4_OK) return s;
+    if ((m_out && !aligned16(m_out)) || (v_out && !aligned16(v_out))) return ADAMW4_EALIGN;
+    std::vector<TensorDesc> descs(1);
+    descs[0] = make_desc(*t, 0);
+    descs[0].aux0 = m_out;
+    descs[0].aux1 = v_out;
+    return run_aux(std::move(descs), false, mode, stream);
+}
+
+const char* adamw4_status_string(int32_t status) {
+    switch (status) {
+    case ADAMW4_OK: return "ok";
+    case ADAMW4_EINVAL: return "invalid argument";
+    case ADAMW4_EALIGN: return "device pointer not 16-byte aligned";
+    case ADAMW4_ESIZE: return "size out of range or state buffer too small";
+    case ADAMW4_EHIP: return "HIP runtime error";
+    case ADAMW4_ENOMEM: return "out of device memory for internal tables";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// adamw4_internal.h -- layout of the device-side work description shared by the HIP kernels
+// (adamw4_kernels.hip) and the host runtime (adamw4_api.cpp).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace adamw4 {
+
+constexpr int kBlock = 128;              // values per FP32 block scale
+constexpr int kLanes = 16;               // lanes that share one 128-value block (a DPP row)
+constexpr int kPerLane = 8;              // consecutive values held by one lane
+constexpr int kWG = 256;                 // threads per workgroup (4 waves of 64)
+constexpr int kRows = kWG / kLanes;      // blocks processed per workgroup iteration
+constexpr int kMinQuant = 4096;          // smaller tensors keep FP32 moments
+
+// descriptor flags
+enum : uint32_t { D_QUANT = 1u, D_HEAD = 2u, D_BF16 = 4u };
+
+// One tensor of a launch.  For quantized tensors s0/s1 are the packed m/v codes and s2/s3 the
+// m/v block scales; for FP32 tensors s0/s1 are the FP32 m/v arrays.  aux0/aux1 carry the
+// initial moments (init) or the decode outputs (decode); unused by the step.
+struct alignas(16) TensorDesc {
+    float* param;
+    const void* grad;
+    void* s0;
+    void* s1;
+    float* s2;
+    float* s3;
+    float* aux0;
+    float* aux1;
+    int64_t numel;
+    uint32_t flags;
+    uint32_t pos;   // position in the caller's list: part of the RNG counter
+};
+
+// A run of up to `chunk_units` consecutive 128-value units of one tensor.
+struct Chunk {
+    uint32_t tensor;
+    uint32_t first_unit;
+};
+
+// Per-step scalars, formed on the host in binary64 and rounded once to FP32.
+struct StepArgs {
+    float step_size;  // lr / (1 - beta1^t)
+    float rs2;        // 1 / sqrt(1 - beta2^t)
+    float decay;      // 1 - lr * wd
+    float omb1;       // 1 - beta1
+    float omb2;       // 1 - beta2
+    float beta1, beta2, eps;
+    uint32_t seed_lo, seed_hi;
+    uint32_t t;
+    int32_t mode;      // v encoder: 0 ZIP-SR, 1 ZE-EDEN
+    int32_t vin_mode;  // codebook of the incoming v
+    int32_t sr_head;   // HEAD tensors' m stochastically rounded this step
+};
+
+struct Launch {
+    const TensorDesc* descs;   // device
+    const Chunk* chunks;       // device
+    uint32_t nchunks;
+    uint32_t chunk_units;
+    int grid;
+};
+
+hipError_t launch_step(const Launch& L, const StepArgs& a, hipStream_t s);
+hipError_t launch_init(const Launch& L, int32_t mode, hipStream_t s);
+hipError_t launch_decode(const Launch& L, int32_t mode, hipStream_t s);
+
+// Resident workgroups per CU of each kernel on the current device (for persistent grids).
+int step_blocks_per_cu();
+int aux_blocks_per_cu();
+
+// Host copies of the compiled-in codebooks (0 NF4, 1 V0, 2 V1).
+void codebook_words(int which, float out[16]);
+
+}  // namespace adamw4

@@ -1,0 +1,147 @@
+/*
+ * adamw4.h -- C ABI of the fused 4-bit AdamW optimizer step (ZIP-SR / ZE-EDEN) on MI355X (gfx950).
+ *
+ * The method: "Rounding in Preconditioner Space: Redesigning 4-bit AdamW Optimizer-State
+ * Quantization" (arXiv 2610.12444), as described on these pages:
+ *   [daiwk-CE]  daiwk.github.io, "ZIP-SR / ZE-EDEN: 4-bit AdamW state quantization",
+ *               section "Core equation" (h(v), ZIP-SR probability, ZE-EDEN rescale, update order)
+ *   [daiwk-PM]  same page, "Paper method and evidence" (decode -> update -> weights -> quantize -> pack)
+ *   [daiwk-LR]  same page, "Local reproduction" (uint8 nibble packing, FP32 block scales,
+ *               FP32 fallback below 4096 elements)
+ *   [lav-ST]    learnaivisually.com, "ZIP-SR 4-bit AdamW" explainer, storage paragraph
+ *               (4-bit m and v, one FP32 scale per 128 values, norm-layer states in FP32)
+ *   [lav-ZE]    same explainer, ZE-EDEN / LM-head paragraph (NF4 for m, LM-head m rounded
+ *               stochastically over the last 10% of training)
+ *   [kc-TC]     kongchang.com explainer, "Two Complementary Technical Approaches"
+ *
+ * Conventions for every entry point:
+ *   - Every call returns an adamw4_status (0 = OK, < 0 = error).  Nothing throws across the ABI.
+ *   - Pointers named "device" are HIP device memory owned by the caller; the library never frees
+ *     or retains them beyond the call's stream-ordered work.  "host" pointers are read during
+ *     the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the device's default stream).  Work is
+ *     enqueued on it and the call returns after enqueueing; results are visible to later work
+ *     on the same stream.  The device is the caller's current HIP device.
+ *   - Argument errors are detected on the host before anything is enqueued, and nothing is
+ *     written when a call returns an error.
+ */
+#ifndef ADAMW4_H
+#define ADAMW4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ADAMW4_OK = 0,
+    ADAMW4_EINVAL = -1, /* bad scalar argument, null pointer, unknown flag/mode/dtype, numel < 1 */
+    ADAMW4_EALIGN = -2, /* a device pointer is not 16-byte aligned */
+    ADAMW4_ESIZE = -3,  /* numel too large, or too many tensors */
+    ADAMW4_EHIP = -4,   /* a HIP runtime call or kernel launch failed (no device, ...) */
+    ADAMW4_ENOMEM = -5  /* the library could not allocate its small internal tables */
+} adamw4_status;
+
+/* v encoder.  ZIP-SR: zero-inclusive 16-level codebook k/15, stochastic choice between the two
+ * levels around v with the preconditioner-space probability [h(v)-h(b)]/[h(a)-h(b)],
+ * h(x) = 1/(sqrt(x/(1-beta2^t)) + eps) ([daiwk-CE], [kc-TC]).  ZE-EDEN: zero-excluding
+ * codebook (k+1)/16, nearest level, then the block scale is multiplied by
+ * |x|^2 / max(<x, Q(x)>, 1e-12 s^2) ([daiwk-CE], [kc-TC]). */
+typedef enum { ADAMW4_ZIP_SR = 0, ADAMW4_ZE_EDEN = 1 } adamw4_mode;
+
+/* per-tensor flags */
+enum {
+    ADAMW4_T_NORM = 1u, /* normalization-layer tensor: m and v stay FP32 ([lav-ST]) */
+    ADAMW4_T_HEAD = 2u  /* LM-head tensor: its m is rounded stochastically when sr_head is set ([lav-ZE]) */
+};
+
+enum { ADAMW4_GRAD_F32 = 0, ADAMW4_GRAD_BF16 = 1 };
+
+/* codebook ids for adamw4_codebook */
+enum { ADAMW4_CB_NF4 = 0, ADAMW4_CB_V0 = 1, ADAMW4_CB_V1 = 2 };
+
+#define ADAMW4_BLOCK 128        /* values per FP32 block scale ([lav-ST]) */
+#define ADAMW4_MIN_QUANT 4096   /* tensors with fewer elements keep FP32 m, v ([daiwk-LR]) */
+#define ADAMW4_MAX_TENSORS 65536
+#define ADAMW4_MAX_NUMEL (((int64_t)1) << 40)
+
+/* One parameter tensor of the step's list.  The tensor's position in the list is part of the
+ * RNG key, so keep the list order fixed across steps. */
+typedef struct {
+    float* param;       /* device, [numel] FP32 master weights, updated in place, 16-B aligned */
+    const void* grad;   /* device, [numel] FP32 or BF16 gradient (read only), 16-B aligned */
+    int64_t numel;      /* 1 .. ADAMW4_MAX_NUMEL */
+    uint32_t flags;     /* ADAMW4_T_NORM | ADAMW4_T_HEAD */
+    uint32_t grad_dtype;/* ADAMW4_GRAD_F32 or ADAMW4_GRAD_BF16 */
+    void* state;        /* device, 16-B aligned, persistent optimizer state of this tensor */
+    size_t state_size;  /* bytes available at `state`; must be >= adamw4_state_bytes(numel, flags)
+                           (ADAMW4_ESIZE otherwise) */
+} adamw4_tensor;
+
+typedef struct {
+    int64_t step;        /* t >= 1: the step being taken (bias corrections, RNG counter) */
+    float lr;            /* finite */
+    float beta1, beta2;  /* each in [0, 1) */
+    float eps;           /* > 0, finite */
+    float weight_decay;  /* finite; decoupled: w <- (1 - lr*wd) w - ... */
+    int32_t mode;        /* adamw4_mode used to encode v this step */
+    int32_t prev_mode;   /* adamw4_mode whose codebook encoded the incoming v; -1 = same as mode */
+    int32_t sr_head;     /* 1: HEAD tensors' m uses stochastic rounding this step (the caller
+                            sets it over the last 10% of training, [lav-ZE]); 0: round to nearest */
+    uint64_t seed;       /* RNG key */
+} adamw4_hparams;
+
+/* Size in bytes of one tensor's persistent optimizer state ([lav-ST], [daiwk-LR]).  Pure host
+ * function, no device needed.  Quantized tensors (numel >= 4096 and not NORM): m codes and v
+ * codes (ceil(numel/2) bytes each, two 4-bit codes per byte, element 2q in the low nibble of
+ * byte q), then m scales and v scales (ceil(numel/128) FP32 each); each section starts on a
+ * 16-byte boundary.  Other tensors: FP32 m then FP32 v (numel each, 16-byte aligned sections).
+ * Returns 0 when numel is outside 1..ADAMW4_MAX_NUMEL. */
+size_t adamw4_state_bytes(int64_t numel, uint32_t flags);
+
+/* Byte offsets of the state's sections (see adamw4_state_bytes): quantized tensors get
+ * {m codes, v codes, m scales, v scales}; FP32 tensors get {m, v, SIZE_MAX, SIZE_MAX}.
+ * offsets: host, 4 entries.  Returns ADAMW4_EINVAL on a bad numel or null pointer. */
+adamw4_status adamw4_state_layout(int64_t numel, uint32_t flags, size_t offsets[4]);
+
+/* The library's 16-word codebooks, copied to host memory `out` (16 floats): NF4 for m
+ * ([lav-ZE], [kc-TC]), V0 = k/15 for ZIP-SR's v, V1 = (k+1)/16 for ZE-EDEN's v ([kc-TC]). */
+adamw4_status adamw4_codebook(int32_t which, float out[16]);
+
+/* Write the initial state of n tensors.  m0[i] / v0[i] are device pointers to numel FP32
+ * initial moments of tensor i (16-B aligned); a NULL array or a NULL entry means zeros.
+ * Non-zero moments are encoded deterministically (absmax scale, nearest level of NF4 for m and
+ * of the codebook of `mode` for v; ZE-EDEN adds its block rescale); no RNG is used because no
+ * step t exists yet.  Only ts[i].numel, flags, state and state_size are used.  m0 and v0 are
+ * host arrays of n pointers.  The call waits for its work on `stream` before returning. */
+adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode,
+                                const float* const* m0, const float* const* v0, void* stream);
+
+/* One fused 4-bit AdamW step over the list of n tensors (the hot path; [daiwk-PM], [daiwk-CE]).
+ * Per element: decode m = NF4[c]*s_m and v = V[c]*s_v (V of prev_mode), m' = b1 m + (1-b1) g,
+ * v' = b2 v + (1-b2) g^2, w' = (1 - lr wd) w - (lr/(1-b1^t)) m' / (sqrt(v')/sqrt(1-b2^t) + eps)
+ * -- weights use the unquantized m', v' -- then per 128-value block: absmax scales, m to NF4
+ * (round to nearest, or state-space stochastic rounding on HEAD tensors when sr_head), v by
+ * ZIP-SR or ZE-EDEN, nibble packing.  FP32 tensors run the same AdamW on FP32 m, v.  Stochastic
+ * choices draw u in [0,1) from Philox4x32-10 keyed by seed with counter
+ * (i>>2, stream<<31 | (i>>2)>>32, tensor position, t); the lower level is kept iff u < p.
+ * ts: host array of n tensors (n = 0 is a no-op).  The whole step is one kernel launch. */
+adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
+                          void* stream);
+
+/* Decode one tensor's state into FP32 moments (test and checkpoint aid): m_out, v_out are
+ * device arrays of t->numel floats, 16-B aligned (either may be NULL).  `mode` names the
+ * codebook that encoded v (the last step's mode).  Waits for its work on `stream`. */
+adamw4_status adamw4_decode_state(const adamw4_tensor* t, int32_t mode, float* m_out,
+                                  float* v_out, void* stream);
+
+/* Static description of a status code. */
+const char* adamw4_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAMW4_H */

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, element by element.
+
+Every case replays single steps: the GPU's inputs are snapshotted, one oracle step runs on the
+snapshot, and the GPU's outputs are compared (codes and scales bit-exact except stochastic
+flips with |u - p| < 1e-6; weights and FP32 moments within 1e-6 relative, reported when not
+bit-exact).  Sizes span several 128-blocks, ragged tails, the 4096-element fallback boundary,
+odd lengths, norm and LM-head tensors, FP32 and BF16 grads, both modes and mode changes.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+f32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_adamw_step_amd as A
+    A.lib()
+    import oracle
+    oracle.build()
+    return A, oracle
+
+
+def test_codebooks_match_oracle(env):
+    A, orc = env
+    for which in range(3):
+        a = np.array(A.codebook(which), f32)
+        assert np.array_equal(a.view(np.uint32), orc.codebook(which).view(np.uint32)), which
+
+
+def test_state_layout_and_bytes(env):
+    A, orc = env
+    for n, f in [(4096, 0), (4097, 0), (4095, 0), (1, 0), (10000, A.T_NORM), (1 << 20, A.T_HEAD)]:
+        off = A.state_layout(n, f)
+        if A.is_quantized(n, f):
+            c, nb = (n + 1) // 2, (n + 127) // 128
+            assert off[0] == 0 and off[1] >= c and off[2] >= off[1] + c and off[3] >= off[2] + 4 * nb
+            assert A.state_bytes(n, f) >= off[3] + 4 * nb
+        else:
+            assert off[1] >= 4 * n and A.state_bytes(n, f) >= off[1] + 4 * n
+        assert all(o % 16 == 0 for o in off if o < 2**63)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_init_matches_oracle(env, mode):
+    """Deterministic encoding of given initial moments (and of zeros) matches the oracle."""
+    import torch
+    from gpu_harness import GpuList, oracle_state, compare_state, say
+    A, orc = env
+    sizes = [4096, 4097, 128 * 37 + 5, 9000, 100, 6000]
+    flags = [0, 0, A.T_HEAD, 0, 0, A.T_NORM]
+    gl = GpuList(sizes, flags, ["f32"] * len(sizes))
+    rng = np.random.default_rng(mode)
+    m0, v0 = [], []
+    for i, n in enumerate(sizes):
+        m = rng.normal(0, 1e-3, n).astype(f32)
+        v = (10 ** rng.uniform(-20, -4, n)).astype(f32)
+        if i == 3:
+            m[:300] = 0
+            v[:300] = 0       # all-zero blocks
+        m0.append(m)
+        v0.append(v)
+    dm0 = [torch.from_numpy(x).cuda() for x in m0]
+    dv0 = [torch.from_numpy(x).cuda() for x in v0]
+    say(f"init mode={mode} sizes={sizes}")
+    gl.pl.init(mode, dm0, [None if i == 1 else x for i, x in enumerate(dv0)])
+    _, _, ss = gl.snapshot()
+    rep = {}
+    for i, n in enumerate(sizes):
+        ref = orc.init_state(n, bool(flags[i] & A.T_NORM), mode, m0[i], None if i == 1 else v0[i])
+        compare_state(f"init{i}", n, oracle_state(ss[i], n, flags[i]), ref, None, rep)
+
+
+def test_decode_matches_oracle(env):
+    import torch
+    from gpu_harness import GpuList, to_np, say
+    A, orc = env
+    sizes = [4096 * 2 + 77, 300]
+    gl = GpuList(sizes, [0, 0], ["f32", "f32"])
+    rng = np.random.default_rng(3)
+    m0 = [rng.normal(0, 1, n).astype(f32) for n in sizes]
+    v0 = [rng.random(n).astype(f32) for n in sizes]
+    gl.pl.init(1, [torch.from_numpy(x).cuda() for x in m0], [torch.from_numpy(x).cuda() for x in v0])
+    for i, n in enumerate(sizes):
+        mo = torch.empty(n, device="cuda")
+        vo = torch.empty(n, device="cuda")
+        say(f"decode tensor {i} n={n}")
+        A.decode_state(gl.pl.array[i], 1, mo.data_ptr(), vo.data_ptr())
+        ref = orc.init_state(n, False, 1, m0[i], v0[i])
+        rm, rv = orc.decode(ref, n, 1)
+        assert np.array_equal(to_np(mo), rm) and np.array_equal(to_np(vo), rv)
+
+
+def _run_steps(env, sizes, flags, gdt, schedule, seed=0, report=None, zero_frac=0.0,
+               hp_extra=None, grad_scale=1e-3):
+    """Run the schedule [(t, mode, prev_mode, sr_head), ...] with single-step replay each step."""
+    from gpu_harness import GpuList, say
+    A, orc = env
+    gl = GpuList(sizes, flags, gdt, seed=seed)
+    gl.pl.init(schedule[0][1])
+    report = {} if report is None else report
+    for (t, mode, prev, srh) in schedule:
+        gl.set_grads(t, seed=seed, zero_frac=zero_frac, scale=grad_scale)
+        kw = dict(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=1234 + seed)
+        kw.update(hp_extra or {})
+        before = gl.snapshot()
+        say(f"step t={t} mode={mode} prev={prev} sr_head={srh} sizes={sizes}")
+        gl.pl.step(A.hparams(**kw))
+        gl.replay_and_compare(before, kw, report, tag=f"t{t}:")
+    return report
+
+
+def test_flat1m_every_step(env):
+    """1,048,576-value FP32 tensor (8192 blocks), FP32 grads, 10 ZIP-SR steps, all replayed."""
+    rep = _run_steps(env, [1 << 20], [0], ["f32"], [(t, 0, -1, 0) for t in range(1, 11)])
+    print(rep)
+
+
+def test_mixed_list_modes(env):
+    """Ragged list: fallback boundary 4095/4096/4097, odd lengths, partial blocks, norm and head
+    tensors, BF16 and FP32 grads; ZIP-SR, then ZE-EDEN (decoding ZIP-SR's codebook), ZE-EDEN,
+    back to ZIP-SR; head SR switched on mid-way."""
+    A = env[0]
+    sizes = [4095, 4096, 4097, 128 * 50 + 3, 64, 1, 7000, 128 * 200, 33333]
+    flags = [0, 0, 0, 0, 0, 0, A.T_NORM, A.T_HEAD, 0]
+    gdt = ["f32", "bf16", "f32", "bf16", "f32", "bf16", "bf16", "bf16", "f32"]
+    sched = [(1, 0, -1, 0), (2, 0, -1, 1), (3, 1, 0, 1), (4, 1, -1, 0), (5, 0, 1, 1), (6, 0, -1, 1)]
+    rep = _run_steps(env, sizes, flags, gdt, sched, seed=1)
+    print({k: v for k, v in rep.items() if "flips" in k and v})
+
+
+def test_edge_cases(env):
+    """Zero gradients (all-zero blocks), 30% exact zeros, beta2 = 0.95 as on the worked example,
+    a late step (bias corrections ~1), tiny gradients (denormal-range v)."""
+    A = env[0]
+    sizes = [4096, 128 * 9 + 1, 200]
+    flags = [0, A.T_HEAD, 0]
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 1), (2, 1, 0, 1)], seed=2, grad_scale=0.0)
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 0), (2, 0, -1, 1)], seed=3, zero_frac=0.3)
+    _run_steps(env, sizes, flags, ["bf16"] * 3, [(1, 0, -1, 0), (2, 1, 0, 0)], seed=4,
+               hp_extra=dict(beta2=0.95, eps=1e-8))
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1000000, 0, -1, 1), (1000001, 1, 0, 1)], seed=5)
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 0), (2, 1, 0, 1), (3, 0, 1, 0)], seed=6,
+               grad_scale=1e-19)
+
+
+def test_run_twice_bit_identical(env):
+    """Same inputs, same step: identical bits (no race in the block reductions)."""
+    import torch
+    from gpu_harness import GpuList, say
+    A, orc = env
+    sizes = [128 * 301 + 7, 5000]
+    gl = GpuList(sizes, [A.T_HEAD, 0], ["bf16", "f32"], seed=9)
+    gl.pl.init(0)
+    gl.set_grads(1, seed=9)
+    hp = A.hparams(step=1, sr_head=1, seed=5)
+    gl.pl.step(hp)
+    gl.set_grads(2, seed=9)
+    p0 = [p.clone() for p in gl.params]
+    s0 = [s.clone() for s in gl.pl.states]
+    outs = []
+    for rep in range(2):
+        for p, q in zip(gl.params, p0):
+            p.copy_(q)
+        for s, q in zip(gl.pl.states, s0):
+            s.copy_(q)
+        say(f"repeat {rep}")
+        gl.pl.step(A.hparams(step=2, sr_head=1, seed=5))
+        torch.cuda.synchronize()
+        outs.append([x.clone() for x in gl.params + gl.pl.states])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
