@@ -137,6 +137,8 @@ struct Plan {
     std::vector<TensorDesc> descs;  // host copy, also the cache key
     uint32_t nchunks = 0;
     uint32_t chunk_units = 0;
+    uint32_t ntails = 0;
+    size_t tails_off = 0;           // byte offset of the tail list in dbuf
     void* dbuf = nullptr;
     uint64_t last_use = 0;
 };
@@ -177,27 +179,40 @@ uint32_t pick_chunk_units(uint64_t total_units, int cus) {
     return cu;
 }
 
-// Build descriptor and chunk tables and copy them to a fresh device buffer.
-adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan*& out) {
+// Units (128-value blocks) a launch walks for tensor d.  Step plans (split_tails) leave the
+// partial last block of a quantized tensor to the tail list.
+uint64_t plan_units(const TensorDesc& d, bool split_tails) {
+    if (split_tails && (d.flags & D_QUANT)) return uint64_t(d.numel / kBlock);
+    return uint64_t((d.numel + kBlock - 1) / kBlock);
+}
+
+// Build descriptor, chunk and tail tables and copy them to a fresh device buffer.
+adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool split_tails,
+                         Plan*& out) {
     uint64_t total_units = 0;
-    for (const TensorDesc& d : descs) total_units += uint64_t((d.numel + kBlock - 1) / kBlock);
+    for (const TensorDesc& d : descs) total_units += plan_units(d, split_tails);
     const uint32_t cu = pick_chunk_units(total_units, cus);
     std::vector<Chunk> chunks;
+    std::vector<uint32_t> tails;
     uint64_t nch = 0;
-    for (const TensorDesc& d : descs) nch += (uint64_t((d.numel + kBlock - 1) / kBlock) + cu - 1) / cu;
+    for (const TensorDesc& d : descs) nch += (plan_units(d, split_tails) + cu - 1) / cu;
     if (nch > UINT32_MAX) return ADAMW4_ESIZE;
     chunks.reserve(size_t(nch));
     for (size_t i = 0; i < descs.size(); ++i) {
-        const uint64_t units = uint64_t((descs[i].numel + kBlock - 1) / kBlock);
+        const uint64_t units = plan_units(descs[i], split_tails);
         for (uint64_t u = 0; u < units; u += cu) chunks.push_back(Chunk{uint32_t(i), uint32_t(u)});
+        if (split_tails && (descs[i].flags & D_QUANT) && descs[i].numel % kBlock != 0)
+            tails.push_back(uint32_t(i));
     }
     const size_t dbytes = align16(descs.size() * sizeof(TensorDesc));
-    const size_t bytes = dbytes + chunks.size() * sizeof(Chunk);
+    const size_t cbytes = align16(chunks.size() * sizeof(Chunk));
+    const size_t bytes = dbytes + cbytes + tails.size() * sizeof(uint32_t);
     void* dbuf = nullptr;
     if (hipMalloc(&dbuf, std::max<size_t>(bytes, 16)) != hipSuccess) return ADAMW4_ENOMEM;
     std::vector<char> host(bytes);
     std::memcpy(host.data(), descs.data(), descs.size() * sizeof(TensorDesc));
     std::memcpy(host.data() + dbytes, chunks.data(), chunks.size() * sizeof(Chunk));
+    std::memcpy(host.data() + dbytes + cbytes, tails.data(), tails.size() * sizeof(uint32_t));
     // a fresh buffer: a blocking copy orders it before any later use on any stream
     if (hipMemcpy(dbuf, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(dbuf);
@@ -208,6 +223,8 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan
     p->descs = std::move(descs);
     p->nchunks = uint32_t(chunks.size());
     p->chunk_units = cu;
+    p->ntails = uint32_t(tails.size());
+    p->tails_off = dbytes + cbytes;
     p->dbuf = dbuf;
     out = p;
     return ADAMW4_OK;
@@ -226,6 +243,8 @@ Launch launch_of(const Plan& p, int grid_cap) {
     L.nchunks = p.nchunks;
     L.chunk_units = p.chunk_units;
     L.grid = int(std::min<uint64_t>(p.nchunks, uint64_t(std::max(grid_cap, 1))));
+    L.tails = reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.dbuf) + p.tails_off);
+    L.ntails = p.ntails;
     return L;
 }
 
@@ -242,7 +261,7 @@ adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan*&
         }
     }
     Plan* p = nullptr;
-    adamw4_status s = build_plan(std::move(descs), dev, cus, p);
+    adamw4_status s = build_plan(std::move(descs), dev, cus, true, p);
     if (s != ADAMW4_OK) return s;
     if (g_plans.size() >= size_t(kMaxPlans)) {
         auto lru = std::min_element(g_plans.begin(), g_plans.end(),
@@ -320,7 +339,7 @@ static adamw4_status run_aux(std::vector<TensorDesc>&& descs, bool init, int32_t
     DeviceInfo di;
     if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
     Plan* p = nullptr;
-    if ((s = build_plan(std::move(descs), dev, di.cus, p)) != ADAMW4_OK) return s;
+    if ((s = build_plan(std::move(descs), dev, di.cus, false, p)) != ADAMW4_OK) return s;
     const Launch L = launch_of(*p, di.cus * di.aux_bpc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = init ? launch_init(L, mode, st) : launch_decode(L, mode, st);

@@ -61,6 +61,11 @@ struct Launch {
     uint32_t nchunks;
     uint32_t chunk_units;
     int grid;
+    // Step launches only: quantized tensors whose last 128-value block is partial.  Their full
+    // blocks are in the chunk table; the partial blocks go to a second, small launch so the
+    // hot kernel carries no per-value tail guards.
+    const uint32_t* tails;     // device, tensor indices
+    uint32_t ntails;
 };
 
 hipError_t launch_step(const Launch& L, const StepArgs& a, hipStream_t s);
