@@ -1,0 +1,153 @@
+"""Parity at the benchmark workloads' full sizes, in the launch configuration bench.py times:
+the whole parameter list is stepped on the GPU, and at selected steps sampled 128-value blocks
+of every quantized tensor (first, last and random blocks, 64 per tensor) plus every FP32-state
+tensor are replayed on the oracle from a snapshot taken just before the step.
+
+Lists (workloads module): GPT 130M-shape (ZIP-SR, BF16 row-scaled grads), GPT 834M-shape
+(ZE-EDEN, v pre-seeded 10^U(-20,-4) through the init encoder), Llama 2.7B-shape (ZIP-SR,
+LM-head stochastic rounding switched on at t = 181 of 200), and the stress list (one 2^30-value
+tensor + 2000 FP32-state tensors, Student-t grads with 30% zeros, ZIP-SR / ZE-EDEN alternating).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS_PER_TENSOR = 64
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_adamw_step_amd as A
+    A.lib()
+    import oracle
+    oracle.build()
+    return A, oracle
+
+
+def _setup(w, A):
+    import torch
+    import workloads as W
+    dev = torch.device("cuda:0")
+    params = [W.make_param(s, i, dev) for i, s in enumerate(w.specs)]
+    grads = [W.make_grad(w, s, i, 1, dev) for i, s in enumerate(w.specs)]
+    pl = A.ParamList(params, grads, [s.flags for s in w.specs])
+    v0 = None
+    if w.v0_kind != "zeros":
+        v0 = [W.make_v0(w, s, i, dev) for i, s in enumerate(w.specs)]
+    pl.init(w.mode_at(1), None, v0)
+    torch.cuda.synchronize()
+    return pl, v0
+
+
+def _samples(w, A, rng):
+    out = []
+    for i, s in enumerate(w.specs):
+        n = s.numel
+        if not A.is_quantized(n, s.flags):
+            out.append((i, 0, n))                       # whole FP32-state tensor
+            continue
+        nb = (n + 127) // 128
+        picks = {0, nb - 1} | set(rng.integers(0, nb, BLOCKS_PER_TENSOR - 2).tolist())
+        for b in sorted(picks):
+            e0 = 128 * b
+            out.append((i, e0, min(128, n - e0)))
+    return out
+
+
+def _grab(pl, A, w, i, e0, cnt):
+    """Host copies of (w, g, state section slices) for elements [e0, e0+cnt) of tensor i."""
+    import torch
+    from gpu_harness import to_np
+    import oracle as orc
+    s = w.specs[i]
+    n = s.numel
+    wv = to_np(pl.params[i][e0:e0 + cnt]).copy()
+    gv = to_np(pl.grads[i][e0:e0 + cnt]).copy()
+    buf = pl.states[i]
+    off = A.state_layout(n, s.flags)
+    if A.is_quantized(n, s.flags):
+        b0, nb = e0 // 128, (cnt + 127) // 128
+        c0, c1 = e0 // 2, (e0 + cnt + 1) // 2
+        sl = lambda o, a, z: to_np(buf[o + a:o + z]).copy()
+        st = orc.State(True, sl(off[0], c0, c1), sl(off[1], c0, c1),
+                       sl(off[2], 4 * b0, 4 * (b0 + nb)).view(np.float32),
+                       sl(off[3], 4 * b0, 4 * (b0 + nb)).view(np.float32))
+    else:
+        st = orc.State(False, m=to_np(buf[off[0]:off[0] + 4 * n]).view(np.float32).copy(),
+                       v=to_np(buf[off[1]:off[1] + 4 * n]).view(np.float32).copy())
+    return wv, gv, st
+
+
+def _run(env, wname, replay_ts):
+    import torch
+    import workloads as W
+    from gpu_harness import compare_state, compare_weights, say
+    A, orc = env
+    w = W.WORKLOADS[wname]
+    say(f"fullsize {wname}: {len(w.specs)} tensors, {w.numel} values")
+    pl, v0 = _setup(w, A)
+    rng = np.random.default_rng(17)
+    samples = _samples(w, A, rng)
+    report = {}
+    if v0 is not None:   # the init encoder on the sampled blocks
+        for (i, e0, cnt) in samples:
+            s = w.specs[i]
+            if not A.is_quantized(s.numel, s.flags):
+                continue
+            _, _, st = _grab(pl, A, w, i, e0, cnt)
+            ref = orc.State(True, np.zeros_like(st.mcodes), np.zeros_like(st.vcodes),
+                            np.zeros_like(st.mscale), np.zeros_like(st.vscale))
+            v0h = v0[i][e0:e0 + cnt].cpu().numpy()
+            orc.lib().orc_encode_init(None, v0h.ctypes.data, s.numel, e0, cnt, w.mode_at(1),
+                                      ref.mcodes.ctypes.data, ref.vcodes.ctypes.data,
+                                      ref.mscale.ctypes.data, ref.vscale.ctypes.data)
+            compare_state(f"init:{i}@{e0}", cnt, st, ref, None, report)
+    del v0
+    prev = w.mode_at(1)
+    last = max(replay_ts)
+    for t in range(1, last + 1):
+        mode = w.mode_at(t)
+        kw = dict(step=t, mode=mode, prev_mode=prev, sr_head=w.sr_head_at(t), seed=0)
+        prev = mode
+        if t in replay_ts:
+            before = [(i, e0, cnt) + _grab(pl, A, w, i, e0, cnt) for (i, e0, cnt) in samples]
+            say(f"  replay t={t} mode={mode} sr_head={kw['sr_head']} ({len(samples)} samples)")
+        pl.step(A.hparams(**kw))
+        if t not in replay_ts:
+            continue
+        torch.cuda.synchronize()
+        for (i, e0, cnt, wv, gv, st) in before:
+            s = w.specs[i]
+            dbg = orc.step_tensor(wv, gv, st, orc.HParams(**kw), pos=i, head=bool(s.flags & 2),
+                                  e0=e0, n=s.numel, dbg=True)
+            w_now, _, st_now = _grab(pl, A, w, i, e0, cnt)
+            name = f"{wname}:t{t}:{i}@{e0}"
+            compare_weights(name, w_now, wv, report)
+            compare_state(name, cnt, st_now, st, dbg, report)
+    flips = sum(v for k, v in report.items() if k.endswith("_flips"))
+    exact = all(v for k, v in report.items() if k.endswith("_bitexact"))
+    say(f"  {wname}: permitted stochastic flips {flips}, weights/FP32 states bit-exact {exact}")
+
+
+@pytest.mark.timeout(900)
+def test_llama2b7_full(env):
+    _run(env, "llama2b7", {1, 2, 180, 181, 200})
+
+
+@pytest.mark.timeout(900)
+def test_gpt130m_full(env):
+    _run(env, "gpt130m", {1, 2, 50, 100})
+
+
+@pytest.mark.timeout(900)
+def test_gpt834m_full(env):
+    _run(env, "gpt834m", {1, 2, 25, 50})
+
+
+@pytest.mark.timeout(900)
+def test_stress_full(env):
+    _run(env, "stress", {1, 2, 3, 20})

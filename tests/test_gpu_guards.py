@@ -1,0 +1,96 @@
+"""Out-of-bounds guard: every parameter, gradient and state buffer lives inside a larger device
+allocation whose surrounding bytes hold a random pattern; after steps in both modes (ragged
+lengths, FP32-state tensors, LM-head stochastic rounding, init and decode) the pattern must be
+intact and the results must still match the oracle."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096   # bytes of canary on each side
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_adamw_step_amd as A
+    A.lib()
+    import oracle
+    oracle.build()
+    return A, oracle
+
+
+class Guarded:
+    """A device byte buffer with `nbytes` usable bytes (16-B aligned) between two canaries."""
+
+    def __init__(self, nbytes, rng):
+        import torch
+        self.n = nbytes
+        self.total = GUARD + ((nbytes + 15) // 16) * 16 + GUARD
+        host = rng.integers(0, 256, self.total, dtype=np.uint8)
+        self.pattern = host.copy()
+        self.buf = torch.from_numpy(host).cuda()
+
+    def view(self, dtype, count):
+        return self.buf[GUARD:GUARD + self.n].view(dtype)[:count]
+
+    def intact(self):
+        import torch
+        torch.cuda.synchronize()
+        h = self.buf.cpu().numpy()
+        lo = np.array_equal(h[:GUARD], self.pattern[:GUARD])
+        hi = np.array_equal(h[GUARD + self.n:], self.pattern[GUARD + self.n:])
+        return lo and hi
+
+
+def test_no_writes_outside_buffers(env):
+    import torch
+    from gpu_harness import oracle_state, compare_state, compare_weights, say, to_np
+    A, orc = env
+    rng = np.random.default_rng(21)
+    sizes = [4095, 4096, 4097, 128 * 50 + 3, 64, 1, 7000, 128 * 40, 33333, 129]
+    flags = [0, 0, 0, 0, 0, 0, A.T_NORM, A.T_HEAD, A.T_HEAD, 0]
+    gdt = ["f32", "bf16", "bf16", "f32", "bf16", "f32", "bf16", "f32", "bf16", "f32"]
+    guards, params, grads, states, specs = [], [], [], [], []
+    for n, f, gd in zip(sizes, flags, gdt):
+        gp = Guarded(4 * n, rng)
+        gg = Guarded((2 if gd == "bf16" else 4) * n, rng)
+        sb = A.state_bytes(n, f)
+        gs = Guarded(sb, rng)
+        p = gp.view(torch.float32, n)
+        p.copy_(torch.from_numpy(rng.normal(0, 0.02, n).astype(np.float32)))
+        g = gg.view(torch.bfloat16 if gd == "bf16" else torch.float32, n)
+        guards += [gp, gg, gs]
+        params.append(p)
+        grads.append(g)
+        states.append(gs.view(torch.uint8, sb))
+    pl = A.ParamList(params, grads, flags, states=states)
+    m0 = [torch.from_numpy(rng.normal(0, 1e-4, n).astype(np.float32)).cuda() for n in sizes]
+    pl.init(A.ZIP_SR, m0, None)
+    ostates = [orc.init_state(n, bool(f & A.T_NORM), orc.ZIP_SR, m0[i].cpu().numpy(), None)
+               for i, (n, f) in enumerate(zip(sizes, flags))]
+    ws = [to_np(p).copy() for p in params]
+    sched = [(1, 0, -1, 0), (2, 1, 0, 1), (3, 0, 1, 1), (4, 0, -1, 0)]
+    for t, mode, prev, srh in sched:
+        for g in grads:
+            g.copy_(torch.from_numpy(rng.normal(0, 1e-3, g.numel()).astype(np.float32)).to(g.dtype))
+        kw = dict(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=3)
+        gh = [to_np(g).copy() for g in grads]
+        say(f"guarded step t={t} mode={mode}")
+        pl.step(A.hparams(**kw))
+        assert all(gd.intact() for gd in guards), f"canary overwritten at step {t}"
+        rep = {}
+        for i, n in enumerate(sizes):
+            dbg = orc.step_tensor(ws[i], gh[i], ostates[i], orc.HParams(**kw), pos=i,
+                                  head=bool(flags[i] & A.T_HEAD), dbg=True)
+            compare_weights(f"t{t}:{i}", to_np(params[i]), ws[i], rep)
+            compare_state(f"t{t}:{i}", n, oracle_state(to_np(states[i]), n, flags[i]), ostates[i], dbg, rep)
+            ws[i] = to_np(params[i]).copy()          # continue from the GPU's values
+            ostates[i] = oracle_state(to_np(states[i]), n, flags[i])
+    # decode into guarded outputs
+    for i, n in enumerate(sizes):
+        gm, gv = Guarded(4 * n, rng), Guarded(4 * n, rng)
+        A.decode_state(pl.array[i], 0, gm.view(torch.float32, n).data_ptr(), gv.view(torch.float32, n).data_ptr())
+        assert gm.intact() and gv.intact()
