@@ -2,7 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2b7]
 
-One step = one adamw_step launch over the whole parameter list (every value: decode, AdamW,
+One step = one adamw4_step call over the whole parameter list (every value: decode, AdamW,
 weight update, requantize, pack), inputs resident in HBM.  The default workload is the
 Llama-style 2.7B list (291 tensors, BF16 grads, ZIP-SR, LM-head m stochastically rounded in
 the last 10% of a 200-step schedule).  The K timed steps take t = 200/K, 2*200/K, ..., 200, so
@@ -10,14 +10,25 @@ the stochastic-rounding phase has its share of the job.  Prints one JSON line.
 
 roofline: algorithmic bytes per launch (12.125 B per quantized value with BF16 grads: FP32
 weight read+write 8, grad 2, m and v codes read+write 2, four FP32 block scales per 128 values
-0.125; 26 B per FP32-state value) over the mean launch time from HIP events on the launch
-stream.  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters stored in
-profiles/counters_<workload>.json, used only if the kernel source is unchanged since.
-cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+0.125; 26 B per FP32-state value) over the mean launch time from HIP events recorded on the
+launch stream.  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
+scaled by the counters' reading on a copy of known size, stored in
+profiles/counters_<workload>.json and used only while the kernel source is unchanged.
+ceiling: a streaming kernel (libadamw4_ceiling.so) that moves the same bytes per value in the
+same access pattern with trivial arithmetic; its rate is the practical HBM ceiling for this
+byte mix on the GPU at hand.
+cpu_baseline: the CPU oracle (test infrastructure, timed here only) stepping the same list,
+tensor by tensor from host copies of the GPU's current state, until a time budget is spent.
+
+python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR [--workload W]
+reads rocprofv3 CSV output (kernel trace + stats, FETCH_SIZE pass, WRITE_SIZE pass, each from
+a run with --copy-calibration), prints a text summary and writes profiles/counters_<W>.json.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
 import hashlib
 import json
 import os
@@ -30,6 +41,9 @@ sys.path.insert(0, ROOT)
 METRIC = "optimizer-step G params/s and achieved HBM GB/s (% of peak), 2.7B list"
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "bit_adamw_step_amd", "csrc", "adamw4_kernels.hip")
+CEILING_LIB = os.path.join(ROOT, "bit_adamw_step_amd", "libadamw4_ceiling.so")
+STEP_KERNEL = "adamw4::step_kernel"
+CALIB_BYTES = 4 << 30          # the --copy-calibration copy: 4 GiB read + 4 GiB written
 
 
 def kernel_hash() -> str:
@@ -49,6 +63,14 @@ def algorithmic_bytes(w) -> tuple[int, int, int]:
     qbytes = q * (8 + gb + 2) + nblk * 16     # w r/w, grad, codes r/w, 4 scale words per block
     fbytes = f * (8 + gb + 16)                # w r/w, grad, FP32 m and v r/w
     return qbytes + fbytes, q, f
+
+
+def pct(xs, p):
+    s = sorted(xs)
+    k = (len(s) - 1) * p / 100.0
+    lo = int(k)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (k - lo)
 
 
 def setup(w, device):
@@ -105,21 +127,58 @@ def run_gpu(w, steps: int, warmup: int, device):
     return pl, ts, per, wall
 
 
-def cpu_baseline(w, pl, budget_s: float = 15.0):
-    """The oracle (unchanged) on a bounded sample of the workload: the first blocks of every
-    quantized tensor, in rounds, until about budget_s of CPU time; plus every FP32-state tensor
-    once.  Returns the oracle's throughput on that sample."""
+def ceiling(q: int, device, reps: int = 5) -> dict | None:
+    """Time the same-byte-mix streaming kernel over q quantized values in flat buffers."""
+    import torch
+    if not os.path.exists(CEILING_LIB) or q < 128:
+        return None
+    L = ctypes.CDLL(CEILING_LIB)
+    P = ctypes.c_void_p
+    L.adamw4_ceiling_mix.argtypes = [P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_int32, P]
+    L.adamw4_ceiling_mix.restype = ctypes.c_int
+    nb = q // 128
+    n = nb * 128
+    wv = torch.zeros(n, dtype=torch.float32, device=device)
+    g = torch.zeros(n, dtype=torch.bfloat16, device=device)
+    mc = torch.zeros(n // 8, dtype=torch.int32, device=device)
+    vc = torch.zeros(n // 8, dtype=torch.int32, device=device)
+    sm = torch.ones(nb, dtype=torch.float32, device=device)
+    sv = torch.ones(nb, dtype=torch.float32, device=device)
+    stream = torch.cuda.current_stream()
+    grid, chunk = 1024, 256
+    args = [wv.data_ptr(), g.data_ptr(), mc.data_ptr(), vc.data_ptr(), sm.data_ptr(), sv.data_ptr(),
+            nb, grid, chunk, ctypes.c_void_p(stream.cuda_stream)]
+    for _ in range(2):
+        if L.adamw4_ceiling_mix(*args) != 0:
+            raise RuntimeError("ceiling kernel launch failed")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        L.adamw4_ceiling_mix(*args)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    byts = n * 12 + nb * 16
+    del wv, g, mc, vc, sm, sv
+    torch.cuda.empty_cache()
+    return {"kernel": "same-byte-mix streaming (12.125 B/value, step access pattern)",
+            "values": n, "ms": round(ms, 4), "GBs": round(byts / (ms / 1000) / 1e9, 1),
+            "grid": grid, "chunk_blocks": chunk}
+
+
+def cpu_baseline(w, pl, budget_s: float = 30.0):
+    """The oracle, unchanged, stepping the workload's tensors in list order from host copies of
+    the GPU's current state (copies not timed) until about budget_s of oracle time, at the last
+    step of the schedule.  Also times the oracle on one thread over the first 4M values."""
     import numpy as np
     import torch
     import oracle as orc
     import bit_adamw_step_amd as A
     orc.build()
+    L = orc.lib()
+    threads = L.orc_threads()
     specs = w.specs
-    quant = [i for i, s in enumerate(specs) if A.is_quantized(s.numel, s.flags)]
-    fp = [i for i, s in enumerate(specs) if not A.is_quantized(s.numel, s.flags)]
-    per_tensor = 128 * 512                        # 65,536 values (512 blocks) per sampled tensor
-    t_total = 0.0
-    n_total = 0
     hp = orc.HParams(step=w.steps, mode=w.mode_at(w.steps), sr_head=w.sr_head_at(w.steps), seed=0)
 
     def host(i, e0, cnt):
@@ -143,35 +202,37 @@ def cpu_baseline(w, pl, budget_s: float = 15.0):
                            v=buf[off[1]:off[1] + 4 * n].cpu().numpy().view(np.float32).copy())
         return w_, g, st
 
-    for i in fp:
-        w_, g, st = host(i, 0, specs[i].numel)
+    def run(i, e0, cnt):
+        w_, g, st = host(i, e0, cnt)
         t0 = time.perf_counter()
-        orc.step_tensor(w_, g, st, hp, pos=i)
-        t_total += time.perf_counter() - t0
-        n_total += specs[i].numel
-    rnd = 0
-    while t_total < budget_s and rnd < 64:
-        for i in quant:
-            n = specs[i].numel
-            e0 = min(rnd * per_tensor, ((n - 1) // 128) * 128)
-            cnt = min(per_tensor, n - e0)
-            w_, g, st = host(i, e0, cnt)
-            t0 = time.perf_counter()
-            orc.step_tensor(w_, g, st, hp, pos=i, head=bool(specs[i].flags & 2), e0=e0, n=n)
-            t_total += time.perf_counter() - t0
-            n_total += cnt
-            if t_total >= budget_s:
-                break
-        rnd += 1
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": round(n_total / t_total / 1e9, 6), "unit": "Gparams/s", "cores": cores,
+        orc.step_tensor(w_, g, st, hp, pos=i, head=bool(specs[i].flags & 2), e0=e0, n=specs[i].numel)
+        return time.perf_counter() - t0
+
+    t_total, n_total, done = 0.0, 0, 0
+    for i, s in enumerate(specs):
+        if t_total >= budget_s:
+            break
+        t_total += run(i, 0, s.numel)
+        n_total += s.numel
+        done += 1
+    # one thread, for scale
+    q0 = next(i for i, s in enumerate(specs) if A.is_quantized(s.numel, s.flags))
+    cnt1 = min(specs[q0].numel, 1 << 22)
+    L.orc_set_threads(1)
+    try:
+        t1 = run(q0, 0, cnt1)
+    finally:
+        L.orc_set_threads(threads)
+    whole = done == len(specs)
+    what = ("the whole list" if whole else f"the first {done} of {len(specs)} tensors")
+    return {"value": round(n_total / t_total / 1e9, 6), "unit": "Gparams/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_total} values ({len(fp)} FP32-state tensors whole, leading 512-block "
-                      f"slices of the quantized tensors), one oracle step at t={w.steps}, "
-                      f"{t_total:.1f} s of oracle time"}
+            "sample": f"{what} ({n_total} values), one oracle step at t={w.steps} from the GPU's "
+                      f"state, {t_total:.1f} s of oracle time on {threads} threads",
+            "value_1thread": round(cnt1 / t1 / 1e9, 6)}
 
 
-def traffic_from_profile(wname: str, bytes_alg: int):
+def traffic_from_profile(wname: str):
     path = os.path.join(ROOT, "profiles", f"counters_{wname}.json")
     if not os.path.exists(path):
         return None
@@ -181,6 +242,78 @@ def traffic_from_profile(wname: str, bytes_alg: int):
     return d.get("hbm_bytes_per_launch")
 
 
+# ---------------------------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------------------------
+
+def _csv(d: str, name: str) -> list[dict]:
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(name):
+                return list(csv.DictReader(open(os.path.join(root, f))))
+    raise FileNotFoundError(f"no *{name} under {d}")
+
+
+def _is_copy(name: str) -> bool:
+    return "copyBuffer" in name or "copy" in name.lower() and "adamw4" not in name
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, wname: str) -> None:
+    import workloads as W
+    w = W.WORKLOADS[wname]
+    bytes_alg, q, f = algorithmic_bytes(w)
+    stats = _csv(trace_dir, "kernel_stats.csv")
+    trace = _csv(trace_dir, "kernel_trace.csv")
+    step = [r for r in trace if STEP_KERNEL in r["Kernel_Name"]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in step]
+    print(f"## rocprofv3 kernel trace ({wname}: {w.numel} values, {len(w.specs)} tensors)\n")
+    print("| kernel | calls | avg ms | min ms | max ms | share % |")
+    print("|---|---|---|---|---|---|")
+    for r in stats[:8]:
+        nm = r["Name"]
+        nm = nm if len(nm) < 60 else nm[:57] + "..."
+        print(f"| {nm} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+              f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | {r['Percentage']} |")
+    if step:
+        r0 = step[0]
+        avg = sum(durs) / len(durs)
+        print(f"\nstep_kernel: {len(durs)} dispatches, mean {avg:.4f} ms, "
+              f"{int(r0['Grid_Size_X']) // int(r0['Workgroup_Size_X'])} workgroups of "
+              f"{r0['Workgroup_Size_X']} threads, VGPR {r0['VGPR_Count']}, "
+              f"SGPR {r0['SGPR_Count']}, LDS {r0['LDS_Block_Size']} B, scratch {r0['Scratch_Size']} B")
+        print(f"algorithmic bytes per launch {bytes_alg} -> {bytes_alg / (avg / 1000) / 1e9:.1f} GB/s "
+              f"({100 * bytes_alg / (avg / 1000) / 1e9 / PEAK_HBM_GBS:.2f}% of {PEAK_HBM_GBS:.0f})")
+    out = {"workload": wname, "kernel_sha": kernel_hash(), "algorithmic_bytes_per_launch": bytes_alg}
+    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = [r for r in _csv(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:
+            per.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        stepv = [v for nm, v in per.values() if STEP_KERNEL in nm]
+        copyv = [v for nm, v in per.values() if _is_copy(nm)]
+        if not stepv or not copyv:
+            print(f"\n{counter}: step or calibration copy dispatches missing")
+            return
+        cal_kib = max(copyv)                     # the 4 GiB copy is the largest copy dispatch
+        factor = (CALIB_BYTES / 1024) / cal_kib  # true KiB per counted KiB
+        kib = sum(stepv) / len(stepv)
+        out[f"{label}_kib_per_dispatch_raw"] = kib
+        out[f"{label}_calibration_copy_kib_raw"] = cal_kib
+        out[f"{label}_calibration_factor"] = factor
+        out[f"{label}_bytes_per_launch"] = kib * 1024 * factor
+        print(f"\n{counter}: step_kernel {len(stepv)} dispatches, mean {kib:.1f} KiB raw; "
+              f"calibration copy of {CALIB_BYTES} B {'read' if label == 'fetch' else 'written'} "
+              f"counted {cal_kib:.1f} KiB -> factor {factor:.4f}; "
+              f"step {kib * 1024 * factor / 1e9:.3f} GB per launch")
+    out["hbm_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    print(f"\nHBM traffic per launch {out['hbm_bytes_per_launch'] / 1e9:.3f} GB vs algorithmic "
+          f"{bytes_alg / 1e9:.3f} GB (ratio {out['hbm_bytes_per_launch'] / bytes_alg:.4f})")
+    path = os.path.join(ROOT, "profiles", f"counters_{wname}.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    json.dump(out, open(path, "w"), indent=1)
+    print(f"wrote {os.path.relpath(path, ROOT)}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,10 +321,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2b7")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 4 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the 4-bit AdamW step needs no communication and every "
               "box here has a single MI355X; run with --gpus 1.", file=sys.stderr)
@@ -206,13 +344,15 @@ def main():
     w = W.WORKLOADS[args.workload]
     print(f"# setup {w.name}: {len(w.specs)} tensors, {w.numel} values", file=sys.stderr, flush=True)
     pl, ts, per, wall = run_gpu(w, args.steps, args.warmup, device)
+    print(f"# timed {len(per)} steps: mean {sum(per) / len(per):.4f} ms", file=sys.stderr, flush=True)
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.float32, device=device)
+        a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=device)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+        torch.cuda.empty_cache()
     bytes_alg, q, f = algorithmic_bytes(w)
     ms = sum(per) / len(per)
     ms_wall = wall * 1000 / len(per)
@@ -220,6 +360,10 @@ def main():
     achieved = bytes_alg / (ms / 1000) / 1e9
     sr = [p for t, p in zip(ts, per) if w.sr_head_at(t)]
     rtn = [p for t, p in zip(ts, per) if not w.sr_head_at(t)]
+    ceil = None if args.no_ceiling else ceiling(q, device)
+    if ceil:
+        ceil["step_frac_of_ceiling"] = round(achieved / ceil["GBs"], 4)
+        print(f"# ceiling {ceil['GBs']} GB/s", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC,
         "value": round(gparams, 3),
@@ -237,6 +381,8 @@ def main():
             "workload": w.name, "values": w.numel, "tensors": len(w.specs),
             "quantized_values": q, "fp32_state_values": f, "grad_dtype": w.grad_dtype,
             "v_mode": w.mode_schedule, "timed_t": [ts[0], ts[-1]],
+            "ms_launch_median": round(pct(per, 50), 4), "ms_launch_p10": round(pct(per, 10), 4),
+            "ms_launch_p90": round(pct(per, 90), 4),
             "ms_launch_rtn_phase": round(sum(rtn) / len(rtn), 4) if rtn else None,
             "ms_launch_sr_head_phase": round(sum(sr) / len(sr), 4) if sr else None,
             "algorithmic_bytes_per_launch": bytes_alg,
@@ -245,7 +391,8 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profile(w.name, bytes_alg)},
+                     "traffic": traffic_from_profile(w.name)},
+        "ceiling": ceil,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

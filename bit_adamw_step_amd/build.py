@@ -1,4 +1,6 @@
-"""Build the HIP library libadamw4.so in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950: libadamw4.so (the optimizer, C ABI in
+include/adamw4.h) and libadamw4_ceiling.so (a measurement kernel the benchmark runs beside the
+step: the practical HBM ceiling for the step's byte mix).
 
 Flags: -ffp-contract=off keeps one rounding per FP32 operation in the code paths that decide
 stored bits (clang-HIP's defaults already give correctly rounded division and square root and
@@ -15,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libadamw4.so")
 SOURCES = [os.path.join(CSRC, "adamw4_kernels.hip"), os.path.join(CSRC, "adamw4_api.cpp")]
+CEILING_LIB = os.path.join(HERE, "libadamw4_ceiling.so")
+CEILING_SOURCES = [os.path.join(CSRC, "stream_ceiling.hip")]
 ARCH = os.environ.get("ADAMW4_OFFLOAD_ARCH", "gfx950")
 
 
@@ -28,17 +32,22 @@ def flags() -> list[str]:
             "-Wall", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libadamw4.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + ["-shared", "-o", tmp] + SOURCES
+def _compile(out: str, sources: list[str], verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + flags() + ["-shared", "-o", tmp] + sources
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     if verbose and (r.stdout or r.stderr):
         print(r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libadamw4.so and libadamw4_ceiling.so (always recompiles)."""
+    _compile(CEILING_LIB, CEILING_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -127,7 +127,9 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
  * ZIP-SR or ZE-EDEN, nibble packing.  FP32 tensors run the same AdamW on FP32 m, v.  Stochastic
  * choices draw u in [0,1) from Philox4x32-10 keyed by seed with counter
  * (i>>2, stream<<31 | (i>>2)>>32, tensor position, t); the lower level is kept iff u < p.
- * ts: host array of n tensors (n = 0 is a no-op).  The whole step is one kernel launch. */
+ * ts: host array of n tensors (n = 0 is a no-op).  The whole list is one kernel launch, plus
+ * one small launch for the partial last blocks when a quantized tensor's numel is not a
+ * multiple of 128. */
 adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
                           void* stream);
 

@@ -99,6 +99,8 @@ def lib():
                                       ctypes.c_int, P, P, P, P]
         L.orc_encode_init.restype = ctypes.c_int
         L.orc_decode.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int, P, P]
+        L.orc_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_encode_block.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_uint64, ctypes.c_int64,
                                        ctypes.c_uint32, ctypes.c_int64, P, P, P]

@@ -48,6 +48,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <xmmintrin.h>
+#include <omp.h>
 
 #define ORC_BLOCK 128
 #define ORC_MIN_QUANT 4096
@@ -518,3 +519,7 @@ void orc_encode_block(const float* x, int nvalid, int rule, float rs2, float eps
     default: encode_v_rtn_block(x, V0, codes, scale); break;
     }
 }
+
+/* Threads the block loops use (OpenMP), and a way to set them: bookkeeping for timing runs. */
+int orc_threads(void) { return omp_get_max_threads(); }
+void orc_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
