@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -77,7 +78,7 @@ adamw4_status check_hparams(const adamw4_hparams& h) {
     if (h.step < 1 || h.step > int64_t(UINT32_MAX)) return ADAMW4_EINVAL;
     if (!(h.beta1 >= 0.0f && h.beta1 < 1.0f)) return ADAMW4_EINVAL;
     if (!(h.beta2 >= 0.0f && h.beta2 < 1.0f)) return ADAMW4_EINVAL;
-    if (!(h.eps > 0.0f) || !finite(h.eps)) return ADAMW4_EINVAL;
+    if (!(h.eps >= FLT_MIN) || !finite(h.eps)) return ADAMW4_EINVAL;   // a normal float
     if (!finite(h.lr) || !finite(h.weight_decay)) return ADAMW4_EINVAL;
     if (h.mode != ADAMW4_ZIP_SR && h.mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
     if (h.prev_mode != -1 && h.prev_mode != ADAMW4_ZIP_SR && h.prev_mode != ADAMW4_ZE_EDEN)

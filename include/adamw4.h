@@ -84,7 +84,7 @@ typedef struct {
     int64_t step;        /* t >= 1: the step being taken (bias corrections, RNG counter) */
     float lr;            /* finite */
     float beta1, beta2;  /* each in [0, 1) */
-    float eps;           /* > 0, finite */
+    float eps;           /* a normal float: >= FLT_MIN (2^-126), finite */
     float weight_decay;  /* finite; decoupled: w <- (1 - lr*wd) w - ... */
     int32_t mode;        /* adamw4_mode used to encode v this step */
     int32_t prev_mode;   /* adamw4_mode whose codebook encoded the incoming v; -1 = same as mode */

@@ -93,6 +93,7 @@ cases = [
   ("beta1 1", step([T()], A.hparams(step=1, beta1=1.0)), EINVAL),
   ("beta2 -0.1", step([T()], A.hparams(step=1, beta2=-0.1)), EINVAL),
   ("eps 0", step([T()], A.hparams(step=1, eps=0.0)), EINVAL),
+  ("eps subnormal", step([T()], A.hparams(step=1, eps=1e-39)), EINVAL),
   ("lr nan", step([T()], A.hparams(step=1, lr=float("nan"))), EINVAL),
   ("wd inf", step([T()], A.hparams(step=1, weight_decay=float("inf"))), EINVAL),
   ("mode 2", step([T()], A.hparams(step=1, mode=2)), EINVAL),
