@@ -136,7 +136,8 @@ def test_mixed_list_modes(env):
 
 def test_edge_cases(env):
     """Zero gradients (all-zero blocks), 30% exact zeros, beta2 = 0.95 as on the worked example,
-    a late step (bias corrections ~1), tiny gradients (denormal-range v)."""
+    a late step (bias corrections ~1), tiny gradients (denormal-range v), and gradients so small
+    that the m block scales fall below 2^-119."""
     A = env[0]
     sizes = [4096, 128 * 9 + 1, 200]
     flags = [0, A.T_HEAD, 0]
@@ -147,6 +148,10 @@ def test_edge_cases(env):
     _run_steps(env, sizes, flags, ["f32"] * 3, [(1000000, 0, -1, 1), (1000001, 1, 0, 1)], seed=5)
     _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 0), (2, 1, 0, 1), (3, 0, 1, 0)], seed=6,
                grad_scale=1e-19)
+    # block scales below 2^-119 but not zero (m' ~ 1e-38, v' underflows): the encoders' small-
+    # scale branch, in both modes and with LM-head stochastic rounding
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 1), (2, 1, 0, 1), (3, 0, 1, 0)], seed=7,
+               grad_scale=1e-37)
 
 
 def test_run_twice_bit_identical(env):
