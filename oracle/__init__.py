@@ -26,9 +26,9 @@ _LIB_OVERRIDE = os.environ.get("ADAMW4_ORACLE_LIB")
 
 BLOCK = 128          # values per FP32 block scale ([lav-ST])
 MIN_QUANT = 4096     # tensors below this stay FP32 ([daiwk-LR])
-ZIP_SR, ZE_EDEN = 0, 1
+ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN = 0, 1, 2, 3, 4
 CB_NF4, CB_V0, CB_V1 = 0, 1, 2
-RULE_M_RTN, RULE_M_SR, RULE_V_ZIP, RULE_V_EDEN, RULE_V_RTN = 0, 1, 2, 3, 4
+RULE_M_RTN, RULE_M_SR, RULE_V_ZIP, RULE_V_EDEN, RULE_V_RTN, RULE_V_SSR, RULE_V_PRTN = 0, 1, 2, 3, 4, 5, 6
 
 
 def build(force: bool = False) -> str:

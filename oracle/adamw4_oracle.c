@@ -39,6 +39,9 @@
  *     ratio of h differences, no underflow for tiny blocks); see orc_zip_p.
  *   - ZE-EDEN: RTN on V1, then gamma = sum(y^2) / max(sum(y * V1[code]), 1e-12), both sums by
  *     a recursive pairwise tree over the 128 zero-padded slots; stored scale gamma * s.
+ *   - the controlled study's other v rules ([lav-RO]) on the zero-inclusive codebook:
+ *     state-space RTN (nearest level), state-space SR (lower level with probability
+ *     (b-y)/(b-a)), preconditioner-space RTN (the level with the nearest h; a tie goes low).
  *   - RNG: Philox4x32-10 (Salmon et al., SC'11) keyed by the seed, counter
  *     (j lo, j hi | stream<<31, tensor position, t) with j = i >> 2; u = (word >> 8) * 2^-24;
  *     the lower level is chosen iff u < p.
@@ -53,7 +56,10 @@
 #define ORC_BLOCK 128
 #define ORC_MIN_QUANT 4096
 
-enum { ORC_ZIP_SR = 0, ORC_ZE_EDEN = 1 };
+/* v encoders: the two methods, and the controlled study's other rules on the zero-inclusive
+ * codebook ([lav-RO]: state-space round-to-nearest and stochastic rounding, preconditioner-space
+ * round-to-nearest) */
+enum { ORC_ZIP_SR = 0, ORC_ZE_EDEN = 1, ORC_V_RTN = 2, ORC_V_SSR = 3, ORC_V_PRTN = 4 };
 enum { ORC_CB_NF4 = 0, ORC_CB_V0 = 1, ORC_CB_V1 = 2 };
 
 typedef struct {
@@ -376,6 +382,57 @@ static void encode_v_rtn_block(const float* x, const float V0[16], uint8_t* code
     }
 }
 
+/* v block, state-space stochastic rounding on the zero-inclusive codebook (the controlled
+ * study's state-space SR, [lav-RO]; the worked example's 75% chance of storing zero): the lower
+ * level of the cell is kept with probability (beta - y)/(beta - alpha), so the mean stored v is
+ * exact.  Same RNG stream and counter as ZIP-SR. */
+static void encode_v_ssr_block(const float* x, int nvalid, const float V0[16], uint64_t seed,
+                               int64_t t, uint32_t pos, int64_t i0, uint8_t* codes, float* scale,
+                               orc_dbg* dbg) {
+    float s = 0.0f;
+    for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);
+    *scale = s;
+    for (int j = 0; j < ORC_BLOCK; ++j) {
+        if (dbg && j < nvalid) { dbg[j].u_v = -1.0f; dbg[j].p_v = -1.0f; }
+        if (s == 0.0f) { codes[j] = 0; continue; }
+        float y = x[j] * inv_scale(s);
+        int k = cell_of(V0, y);
+        float lo = V0[k], hi = V0[k + 1];
+        if (y <= lo) { codes[j] = (uint8_t)k; continue; }
+        if (y >= hi) { codes[j] = (uint8_t)(k + 1); continue; }
+        float p = (hi - y) / (hi - lo);
+        float u = orc_uniform(seed, t, pos, 0, i0 + j);
+        if (dbg && j < nvalid) { dbg[j].u_v = u; dbg[j].p_v = p; }
+        codes[j] = (uint8_t)(u < p ? k : k + 1);
+    }
+}
+
+/* v block, preconditioner-space round to nearest on the zero-inclusive codebook (the controlled
+ * study's deterministic preconditioner-space rule, [lav-RO]): the level whose multiplier h is
+ * nearest to h(v).  h is decreasing, so it is one of the two levels of the cell, and with p the
+ * ZIP-SR lower-level probability h(alpha) - h(v) = (1-p)(h(alpha) - h(beta)) and
+ * h(v) - h(beta) = p (h(alpha) - h(beta)): the lower level is nearer iff p > 1/2; a tie goes to
+ * the lower code.  The debug record carries u = 1/2 as the threshold p is compared with. */
+static void encode_v_prtn_block(const float* x, int nvalid, const float V0[16], float rs2,
+                                float eps, uint8_t* codes, float* scale, orc_dbg* dbg) {
+    float s = 0.0f;
+    for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);
+    *scale = s;
+    float c = sqrtf(s) * rs2;
+    for (int j = 0; j < ORC_BLOCK; ++j) {
+        if (dbg && j < nvalid) { dbg[j].u_v = -1.0f; dbg[j].p_v = -1.0f; }
+        if (s == 0.0f) { codes[j] = 0; continue; }
+        float y = x[j] * inv_scale(s);
+        int k = cell_of(V0, y);
+        float lo = V0[k], hi = V0[k + 1];
+        if (y <= lo) { codes[j] = (uint8_t)k; continue; }
+        if (y >= hi) { codes[j] = (uint8_t)(k + 1); continue; }
+        float p = orc_zip_p(y, lo, hi, c, eps);
+        if (dbg && j < nvalid) { dbg[j].u_v = 0.5f; dbg[j].p_v = p; }
+        codes[j] = (uint8_t)(p >= 0.5f ? k : k + 1);
+    }
+}
+
 /* nibble packing: element 2q in the low nibble of byte q, element 2q+1 in the high nibble;
  * nibbles past the end of the tensor are 0 ([daiwk-LR]: uint8 nibble packing). */
 static void pack_block(const uint8_t* codes, int nvalid, uint8_t* bytes) {
@@ -416,10 +473,12 @@ int orc_step_quant(float* w, const void* g, int g_bf16, int64_t n, int64_t e0, i
                    uint8_t* mcodes, uint8_t* vcodes, float* mscale, float* vscale,
                    int is_head, uint32_t pos, const orc_hparams* hp, float* dbg_out) {
     if (e0 < 0 || cnt < 0 || (e0 % ORC_BLOCK) != 0 || e0 + cnt > n) return -1;
+    if (hp->mode < ORC_ZIP_SR || hp->mode > ORC_V_PRTN) return -1;
     if (cnt == 0) return 0;
     float NF4[16], V0[16], V1[16];
     nf4_table(NF4); v0_table(V0); v1_table(V1);
-    const float* Vin = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZIP_SR) ? V0 : V1;
+    /* ZE-EDEN's codebook excludes zero; every other encoder uses the zero-inclusive one */
+    const float* Vin = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZE_EDEN) ? V1 : V0;
     orc_scalars_t s = scalars_of(hp);
     int sr_m = (is_head && hp->sr_head) ? 1 : 0;
     int64_t nblk = (cnt + ORC_BLOCK - 1) / ORC_BLOCK;
@@ -445,11 +504,20 @@ int orc_step_quant(float* w, const void* g, int g_bf16, int64_t n, int64_t e0, i
             }
             orc_dbg* d = dbg ? dbg + lo : NULL;
             encode_m_block(mw, nvalid, sr_m, NF4, hp->seed, hp->step, pos, e0 + lo, cm, &mscale[b], d);
-            if (hp->mode == ORC_ZIP_SR)
+            switch (hp->mode) {
+            case ORC_ZIP_SR:
                 encode_v_zip_block(vw, nvalid, V0, s.rs2, hp->eps, hp->seed, hp->step, pos, e0 + lo,
                                    cv, &vscale[b], d);
-            else
-                encode_v_eden_block(vw, V1, cv, &vscale[b]);
+                break;
+            case ORC_ZE_EDEN: encode_v_eden_block(vw, V1, cv, &vscale[b]); break;
+            case ORC_V_RTN: encode_v_rtn_block(vw, V0, cv, &vscale[b]); break;
+            case ORC_V_SSR:
+                encode_v_ssr_block(vw, nvalid, V0, hp->seed, hp->step, pos, e0 + lo, cv, &vscale[b], d);
+                break;
+            default:
+                encode_v_prtn_block(vw, nvalid, V0, s.rs2, hp->eps, cv, &vscale[b], d);
+                break;
+            }
             pack_block(cm, nvalid, mcodes + lo / 2);
             pack_block(cv, nvalid, vcodes + lo / 2);
         }
@@ -476,8 +544,8 @@ int orc_encode_init(const float* m0, const float* v0, int64_t n, int64_t e0, int
             vw[j] = (j < nvalid && v0) ? v0[lo + j] : 0.0f;
         }
         encode_m_block(mw, nvalid, 0, NF4, 0, 0, 0, 0, cm, &mscale[b], NULL);
-        if (mode == ORC_ZIP_SR) encode_v_rtn_block(vw, V0, cv, &vscale[b]);
-        else encode_v_eden_block(vw, V1, cv, &vscale[b]);
+        if (mode == ORC_ZE_EDEN) encode_v_eden_block(vw, V1, cv, &vscale[b]);
+        else encode_v_rtn_block(vw, V0, cv, &vscale[b]);
         pack_block(cm, nvalid, mcodes + lo / 2);
         pack_block(cv, nvalid, vcodes + lo / 2);
     }
@@ -490,7 +558,7 @@ void orc_decode(const uint8_t* mcodes, const uint8_t* vcodes, const float* mscal
                 const float* vscale, int64_t cnt, int mode, float* m_out, float* v_out) {
     float NF4[16], V0[16], V1[16];
     nf4_table(NF4); v0_table(V0); v1_table(V1);
-    const float* V = (mode == ORC_ZIP_SR) ? V0 : V1;
+    const float* V = (mode == ORC_ZE_EDEN) ? V1 : V0;
     ieee_mode();
     for (int64_t i = 0; i < cnt; ++i) {
         int64_t b = i / ORC_BLOCK;
@@ -516,6 +584,8 @@ void orc_encode_block(const float* x, int nvalid, int rule, float rs2, float eps
     case 1: encode_m_block(x, nvalid, 1, NF4, seed, t, pos, i0, codes, scale, d); break;
     case 2: encode_v_zip_block(x, nvalid, V0, rs2, eps, seed, t, pos, i0, codes, scale, d); break;
     case 3: encode_v_eden_block(x, V1, codes, scale); break;
+    case 5: encode_v_ssr_block(x, nvalid, V0, seed, t, pos, i0, codes, scale, d); break;
+    case 6: encode_v_prtn_block(x, nvalid, V0, rs2, eps, codes, scale, d); break;
     default: encode_v_rtn_block(x, V0, codes, scale); break;
     }
 }

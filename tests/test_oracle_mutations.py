@@ -40,6 +40,12 @@ MUTANTS = {
                   "const double delta = 0.9677083;"),
     "absmax_not_abs": ("for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, fabsf(x[j]));",
                        "for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);"),
+    "ssr_p_inverted": ("float p = (hi - y) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 0, i0 + j);",
+                       "float p = (y - lo) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 0, i0 + j);"),
+    "prtn_state_space": ("float p = orc_zip_p(y, lo, hi, c, eps);\n        if (dbg && j < nvalid) { dbg[j].u_v = 0.5f;",
+                         "float p = (hi - y) / (hi - lo);\n        if (dbg && j < nvalid) { dbg[j].u_v = 0.5f;"),
+    "prtn_threshold": ("codes[j] = (uint8_t)(p >= 0.5f ? k : k + 1);",
+                       "codes[j] = (uint8_t)(p >= 0.25f ? k : k + 1);"),
 }
 
 

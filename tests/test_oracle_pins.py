@@ -174,7 +174,7 @@ def _quant_tensor(orc, n, rng, head=False, mode=0):
     return w, st
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 def test_step1_weights_equal_fp32_adamw(orc, mode):
     """From m0 = v0 = 0 the quantized state decodes to 0, and weights are updated from the
     unquantized working moments before requantization ([daiwk-CE], [daiwk-PM]), so step-1
@@ -191,7 +191,8 @@ def test_step1_weights_equal_fp32_adamw(orc, mode):
     assert np.array_equal(w.view(np.uint32), w_fp.view(np.uint32))
 
 
-@pytest.mark.parametrize("mode,prev", [(0, -1), (1, -1), (1, 0), (0, 1)])
+@pytest.mark.parametrize("mode,prev", [(0, -1), (1, -1), (1, 0), (0, 1), (2, -1), (3, -1),
+                                       (4, -1), (3, 1), (1, 4), (2, 0)])
 def test_every_step_uses_decoded_state(orc, mode, prev):
     """Each step's weights = FP32 AdamW applied to decode(state) (decode -> update -> weights,
     [daiwk-PM] flowchart); the codebook for decoding is the one that encoded the state."""
@@ -268,6 +269,87 @@ def test_worked_example_monte_carlo(orc):
     sigma = np.sqrt(total * p * (1 - p))
     assert abs(zeros - total * p) < 5 * sigma
     assert abs(hsum / total - h64(1e-12, 1.0, 1e-8)) < 5 * np.sqrt(p) * 1e8 / np.sqrt(total)
+
+
+def test_state_sr_worked_example(orc):
+    """The state-space SR rule of the controlled study on the worked example's block ([lav-RO],
+    worked example): zero is stored with probability (b - v)/b = 75%; the block encoder's p
+    matches it and the stored-zero frequency over seeds is 75% within 5 sigma; the mean stored v
+    is v (the rule is unbiased in state space)."""
+    G = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    V0 = orc.codebook(orc.CB_V0)
+    s = f32(G["level_b"]) / V0[1]
+    x = np.full(128, G["v_true"], f32)
+    x[0] = s
+    zeros = total = 0
+    vsum = 0.0
+    for seed in range(200):
+        codes, scale, dbg = orc.encode_block(x, orc.RULE_V_SSR, seed=seed, t=5)
+        assert scale == s and codes[0] == 15
+        p = dbg[1:, 1]
+        assert np.all(np.abs(p - G["state_sr_prob_zero"]) < 1e-6)
+        zeros += int((codes[1:] == 0).sum())
+        total += 127
+        vsum += (V0[codes[1:]].astype(np.float64) * float(scale)).sum()
+    p0 = G["state_sr_prob_zero"]
+    assert abs(zeros - total * p0) < 5 * np.sqrt(total * p0 * (1 - p0))
+    b = float(V0[1]) * float(s)
+    assert abs(vsum / total - G["v_true"]) < 5 * b * np.sqrt(p0 * (1 - p0) / total)
+
+
+def test_state_sr_unbiased_in_state_space(orc):
+    """State-space SR on random blocks: over seeds the mean decoded v equals v for every element
+    (5 sigma of the binomial spread of its own cell), the mirror image of ZIP-SR's exact mean h."""
+    rng = np.random.default_rng(41)
+    V0 = orc.codebook(orc.CB_V0).astype(np.float64)
+    x = (10 ** rng.uniform(-9, -6, 128)).astype(f32)
+    n = 600
+    acc = np.zeros(128)
+    for seed in range(n):
+        codes, scale, _ = orc.encode_block(x, orc.RULE_V_SSR, seed=seed, t=2, pos=3)
+        acc += V0[codes] * scale
+    mean = acc / n
+    s = float(x.max())
+    y = x.astype(np.float64) / s
+    k = np.clip(np.searchsorted(V0, y, side="right") - 1, 0, 14)
+    width = (V0[k + 1] - V0[k]) * s
+    assert np.all(np.abs(mean - x) <= 5 * width * 0.5 / np.sqrt(n) + 1e-6 * s)
+
+
+def test_prtn_is_nearest_in_preconditioner_space(orc):
+    """Preconditioner-space RTN picks the level whose h = 1/(sqrt(level/bc2) + eps) is nearest to
+    h(v) among all 16 levels (brute force in binary64 over random blocks, scales and bias
+    corrections); it can differ only where the binary64 distances tie to 1e-6 of h(a) - h(b).
+    On the worked example it stores b, never zero."""
+    rng = np.random.default_rng(42)
+    V0 = orc.codebook(orc.CB_V0).astype(np.float64)
+    checked = 0
+    for _ in range(60):
+        s = float(f32(10 ** rng.uniform(-14, -2)))
+        bc2 = float(rng.choice([1e-3, 0.2, 1.0]))
+        rs2 = float(f32(1 / np.sqrt(bc2)))
+        eps = 1e-8
+        x = (rng.uniform(0, 1, 128) ** 3 * s).astype(f32)
+        x[0] = f32(s)
+        codes, scale, dbg = orc.encode_block(x, orc.RULE_V_PRTN, rs2=rs2, eps=eps)
+        h = lambda v: 1.0 / (np.sqrt(v) * rs2 + eps)
+        lv = V0 * float(scale)
+        for j in range(128):
+            hv = h(float(x[j]))
+            dist = np.abs(h(lv) - hv)
+            best = int(np.argmin(dist))
+            if codes[j] != best:
+                k = min(int(codes[j]), best)
+                span = h(lv[k]) - h(lv[k + 1])
+                assert abs(dist[codes[j]] - dist[best]) <= 1e-6 * span, (j, codes[j], best)
+            checked += 1
+    assert checked == 60 * 128
+    G = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    sb = f32(G["level_b"]) / f32(orc.codebook(orc.CB_V0)[1])
+    xw = np.full(128, G["v_true"], f32)
+    xw[0] = sb
+    codes, _, dbg = orc.encode_block(xw, orc.RULE_V_PRTN, rs2=1.0, eps=G["eps"])
+    assert np.all(codes[1:] == 1) and np.all(dbg[1:, 0] == 0.5)
 
 
 def test_closed_form_zero_cell(orc):
