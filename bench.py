@@ -95,16 +95,20 @@ def timed_schedule(w, K: int) -> list[int]:
     return [max(1, round((k + 1) * w.steps / K)) for k in range(K)]
 
 
-def run_gpu(w, steps: int, warmup: int, device):
+V_MODES = {"zip": 0, "eden": 1, "rtn": 2, "ssr": 3, "prtn": 4}
+
+
+def run_gpu(w, steps: int, warmup: int, device, v_mode: str | None = None):
     import torch
     import bit_adamw_step_amd as A
+    mode_at = (lambda t: V_MODES[v_mode]) if v_mode else w.mode_at
     pl = setup(w, device)
     stream = torch.cuda.current_stream()
-    prev = w.mode_at(1)
+    prev = mode_at(1)
 
     def hp(t):
         nonlocal prev
-        m = w.mode_at(t)
+        m = mode_at(t)
         h = A.hparams(step=t, mode=m, prev_mode=prev, sr_head=w.sr_head_at(t), seed=0)
         prev = m
         return h
@@ -320,6 +324,8 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2b7")
+    ap.add_argument("--v-mode", choices=sorted(V_MODES), default=None,
+                    help="v encoder for every step (default: the workload's own schedule)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
@@ -343,7 +349,7 @@ def main():
     device = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
     print(f"# setup {w.name}: {len(w.specs)} tensors, {w.numel} values", file=sys.stderr, flush=True)
-    pl, ts, per, wall = run_gpu(w, args.steps, args.warmup, device)
+    pl, ts, per, wall = run_gpu(w, args.steps, args.warmup, device, args.v_mode)
     print(f"# timed {len(per)} steps: mean {sum(per) / len(per):.4f} ms", file=sys.stderr, flush=True)
     if args.copy_calibration:
         a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=device)
@@ -380,7 +386,7 @@ def main():
         "config": {
             "workload": w.name, "values": w.numel, "tensors": len(w.specs),
             "quantized_values": q, "fp32_state_values": f, "grad_dtype": w.grad_dtype,
-            "v_mode": w.mode_schedule, "timed_t": [ts[0], ts[-1]],
+            "v_mode": args.v_mode or w.mode_schedule, "timed_t": [ts[0], ts[-1]],
             "ms_launch_median": round(pct(per, 50), 4), "ms_launch_p10": round(pct(per, 10), 4),
             "ms_launch_p90": round(pct(per, 90), 4),
             "ms_launch_rtn_phase": round(sum(rtn) / len(rtn), 4) if rtn else None,

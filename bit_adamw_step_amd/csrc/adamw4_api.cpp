@@ -74,15 +74,16 @@ adamw4_status check_tensor_step(const adamw4_tensor& t) {
 
 bool finite(float x) { return std::isfinite(x); }
 
+bool valid_mode(int32_t m) { return m >= ADAMW4_ZIP_SR && m <= ADAMW4_V_PRTN; }
+
 adamw4_status check_hparams(const adamw4_hparams& h) {
     if (h.step < 1 || h.step > int64_t(UINT32_MAX)) return ADAMW4_EINVAL;
     if (!(h.beta1 >= 0.0f && h.beta1 < 1.0f)) return ADAMW4_EINVAL;
     if (!(h.beta2 >= 0.0f && h.beta2 < 1.0f)) return ADAMW4_EINVAL;
     if (!(h.eps >= FLT_MIN) || !finite(h.eps)) return ADAMW4_EINVAL;   // a normal float
     if (!finite(h.lr) || !finite(h.weight_decay)) return ADAMW4_EINVAL;
-    if (h.mode != ADAMW4_ZIP_SR && h.mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
-    if (h.prev_mode != -1 && h.prev_mode != ADAMW4_ZIP_SR && h.prev_mode != ADAMW4_ZE_EDEN)
-        return ADAMW4_EINVAL;
+    if (!valid_mode(h.mode)) return ADAMW4_EINVAL;
+    if (h.prev_mode != -1 && !valid_mode(h.prev_mode)) return ADAMW4_EINVAL;
     if (h.sr_head != 0 && h.sr_head != 1) return ADAMW4_EINVAL;
     return ADAMW4_OK;
 }
@@ -104,7 +105,8 @@ StepArgs step_args(const adamw4_hparams& h) {
     a.seed_hi = uint32_t(h.seed >> 32);
     a.t = uint32_t(h.step);
     a.mode = h.mode;
-    a.vin_mode = (h.prev_mode < 0) ? h.mode : h.prev_mode;
+    // codebook of the incoming v: zero-excluding after ZE-EDEN, zero-inclusive after any other
+    a.vin_mode = (((h.prev_mode < 0) ? h.mode : h.prev_mode) == ADAMW4_ZE_EDEN) ? 1 : 0;
     a.sr_head = h.sr_head;
     return a;
 }
@@ -353,7 +355,7 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
                                 const float* const* m0, const float* const* v0, void* stream) {
     if (n < 0 || (n > 0 && !ts)) return ADAMW4_EINVAL;
     if (n > ADAMW4_MAX_TENSORS) return ADAMW4_ESIZE;
-    if (mode != ADAMW4_ZIP_SR && mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
+    if (!valid_mode(mode)) return ADAMW4_EINVAL;
     adamw4_status s;
     for (int32_t i = 0; i < n; ++i) {
         if ((s = check_tensor_common(ts[i])) != ADAMW4_OK) return s;
@@ -375,7 +377,7 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
 adamw4_status adamw4_decode_state(const adamw4_tensor* t, int32_t mode, float* m_out,
                                   float* v_out, void* stream) {
     if (!t) return ADAMW4_EINVAL;
-    if (mode != ADAMW4_ZIP_SR && mode != ADAMW4_ZE_EDEN) return ADAMW4_EINVAL;
+    if (!valid_mode(mode)) return ADAMW4_EINVAL;
     adamw4_status s = check_tensor_common(*t);
     if (s != ADAMW4_OK) return s;
     if ((m_out && !aligned16(m_out)) || (v_out && !aligned16(v_out))) return ADAMW4_EALIGN;

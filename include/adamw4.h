@@ -48,8 +48,19 @@ typedef enum {
  * levels around v with the preconditioner-space probability [h(v)-h(b)]/[h(a)-h(b)],
  * h(x) = 1/(sqrt(x/(1-beta2^t)) + eps) ([daiwk-CE], [kc-TC]).  ZE-EDEN: zero-excluding
  * codebook (k+1)/16, nearest level, then the block scale is multiplied by
- * |x|^2 / max(<x, Q(x)>, 1e-12 s^2) ([daiwk-CE], [kc-TC]). */
-typedef enum { ADAMW4_ZIP_SR = 0, ADAMW4_ZE_EDEN = 1 } adamw4_mode;
+ * |x|^2 / max(<x, Q(x)>, 1e-12 s^2) ([daiwk-CE], [kc-TC]).
+ * The other three are the rules the method is compared with in the pages' controlled study,
+ * all on the zero-inclusive codebook ([lav-RO]): V_RTN, nearest level in v (ties low);
+ * V_SSR, state-space stochastic rounding (lower level with probability (b-v)/(b-a)); V_PRTN,
+ * preconditioner-space round to nearest (the level with the nearest h, ties low).  A v encoded
+ * by any mode but ZE-EDEN decodes with the zero-inclusive codebook. */
+typedef enum {
+    ADAMW4_ZIP_SR = 0,
+    ADAMW4_ZE_EDEN = 1,
+    ADAMW4_V_RTN = 2,
+    ADAMW4_V_SSR = 3,
+    ADAMW4_V_PRTN = 4
+} adamw4_mode;
 
 /* per-tensor flags */
 enum {
@@ -113,7 +124,8 @@ adamw4_status adamw4_codebook(int32_t which, float out[16]);
 /* Write the initial state of n tensors.  m0[i] / v0[i] are device pointers to numel FP32
  * initial moments of tensor i (16-B aligned); a NULL array or a NULL entry means zeros.
  * Non-zero moments are encoded deterministically (absmax scale, nearest level of NF4 for m and
- * of the codebook of `mode` for v; ZE-EDEN adds its block rescale); no RNG is used because no
+ * of the codebook of `mode` for v, the zero-inclusive one unless `mode` is ZE-EDEN; ZE-EDEN adds
+ * its block rescale); no RNG is used because no
  * step t exists yet.  Only ts[i].numel, flags, state and state_size are used.  m0 and v0 are
  * host arrays of n pointers.  The call waits for its work on `stream` before returning. */
 adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode,
@@ -124,7 +136,7 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
  * v' = b2 v + (1-b2) g^2, w' = (1 - lr wd) w - (lr/(1-b1^t)) m' / (sqrt(v')/sqrt(1-b2^t) + eps)
  * -- weights use the unquantized m', v' -- then per 128-value block: absmax scales, m to NF4
  * (round to nearest, or state-space stochastic rounding on HEAD tensors when sr_head), v by
- * ZIP-SR or ZE-EDEN, nibble packing.  FP32 tensors run the same AdamW on FP32 m, v.  Stochastic
+ * the encoder of hp->mode, nibble packing.  FP32 tensors run the same AdamW on FP32 m, v.  Stochastic
  * choices draw u in [0,1) from Philox4x32-10 keyed by seed with counter
  * (i>>2, stream<<31 | (i>>2)>>32, tensor position, t); the lower level is kept iff u < p.
  * ts: host array of n tensors (n = 0 is a no-op).  The whole list is one kernel launch, plus

@@ -96,8 +96,9 @@ cases = [
   ("eps subnormal", step([T()], A.hparams(step=1, eps=1e-39)), EINVAL),
   ("lr nan", step([T()], A.hparams(step=1, lr=float("nan"))), EINVAL),
   ("wd inf", step([T()], A.hparams(step=1, weight_decay=float("inf"))), EINVAL),
-  ("mode 2", step([T()], A.hparams(step=1, mode=2)), EINVAL),
-  ("prev_mode 3", step([T()], A.hparams(step=1, prev_mode=3)), EINVAL),
+  ("mode 5", step([T()], A.hparams(step=1, mode=5)), EINVAL),
+  ("mode -1", step([T()], A.hparams(step=1, mode=-1)), EINVAL),
+  ("prev_mode 7", step([T()], A.hparams(step=1, prev_mode=7)), EINVAL),
   ("sr_head 2", step([T()], A.hparams(step=1, sr_head=2)), EINVAL),
   ("step > 2^32-1", step([T()], A.hparams(step=1 << 32)), EINVAL),
   ("numel 0", step([T(numel=0)], good), EINVAL),

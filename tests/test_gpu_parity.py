@@ -46,9 +46,10 @@ def test_state_layout_and_bytes(env):
         assert all(o % 16 == 0 for o in off if o < 2**63)
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 def test_init_matches_oracle(env, mode):
-    """Deterministic encoding of given initial moments (and of zeros) matches the oracle."""
+    """Deterministic encoding of given initial moments (and of zeros) matches the oracle; every
+    mode but ZE-EDEN encodes v to the nearest level of the zero-inclusive codebook."""
     import torch
     from gpu_harness import GpuList, oracle_state, compare_state, say
     A, orc = env
@@ -76,7 +77,8 @@ def test_init_matches_oracle(env, mode):
         compare_state(f"init{i}", n, oracle_state(ss[i], n, flags[i]), ref, None, rep)
 
 
-def test_decode_matches_oracle(env):
+@pytest.mark.parametrize("mode", [0, 1, 3])
+def test_decode_matches_oracle(env, mode):
     import torch
     from gpu_harness import GpuList, to_np, say
     A, orc = env
@@ -85,14 +87,14 @@ def test_decode_matches_oracle(env):
     rng = np.random.default_rng(3)
     m0 = [rng.normal(0, 1, n).astype(f32) for n in sizes]
     v0 = [rng.random(n).astype(f32) for n in sizes]
-    gl.pl.init(1, [torch.from_numpy(x).cuda() for x in m0], [torch.from_numpy(x).cuda() for x in v0])
+    gl.pl.init(mode, [torch.from_numpy(x).cuda() for x in m0], [torch.from_numpy(x).cuda() for x in v0])
     for i, n in enumerate(sizes):
         mo = torch.empty(n, device="cuda")
         vo = torch.empty(n, device="cuda")
-        say(f"decode tensor {i} n={n}")
-        A.decode_state(gl.pl.array[i], 1, mo.data_ptr(), vo.data_ptr())
-        ref = orc.init_state(n, False, 1, m0[i], v0[i])
-        rm, rv = orc.decode(ref, n, 1)
+        say(f"decode tensor {i} n={n} mode={mode}")
+        A.decode_state(gl.pl.array[i], mode, mo.data_ptr(), vo.data_ptr())
+        ref = orc.init_state(n, False, mode, m0[i], v0[i])
+        rm, rv = orc.decode(ref, n, mode)
         assert np.array_equal(to_np(mo), rm) and np.array_equal(to_np(vo), rv)
 
 
@@ -131,6 +133,21 @@ def test_mixed_list_modes(env):
     gdt = ["f32", "bf16", "f32", "bf16", "f32", "bf16", "bf16", "bf16", "f32"]
     sched = [(1, 0, -1, 0), (2, 0, -1, 1), (3, 1, 0, 1), (4, 1, -1, 0), (5, 0, 1, 1), (6, 0, -1, 1)]
     rep = _run_steps(env, sizes, flags, gdt, sched, seed=1)
+    print({k: v for k, v in rep.items() if "flips" in k and v})
+
+
+def test_study_modes(env):
+    """The controlled study's other v rules (state-space RTN, state-space SR, preconditioner-
+    space RTN) on the ragged mixed list, alone and switching with ZIP-SR and ZE-EDEN (decoding
+    the previous step's codebook), LM-head SR on and off, FP32 and BF16 grads."""
+    A = env[0]
+    sizes = [4095, 4096, 4097, 128 * 50 + 3, 7000, 128 * 200, 33333]
+    flags = [0, 0, 0, 0, A.T_NORM, A.T_HEAD, 0]
+    gdt = ["f32", "bf16", "f32", "bf16", "bf16", "bf16", "f32"]
+    R, S, P = A.V_RTN, A.V_SSR, A.V_PRTN
+    sched = [(1, R, -1, 0), (2, R, -1, 1), (3, S, R, 1), (4, S, -1, 0), (5, P, S, 0), (6, P, -1, 1),
+             (7, A.ZE_EDEN, P, 0), (8, S, A.ZE_EDEN, 1), (9, A.ZIP_SR, S, 0), (10, R, A.ZIP_SR, 0)]
+    rep = _run_steps(env, sizes, flags, gdt, sched, seed=8)
     print({k: v for k, v in rep.items() if "flips" in k and v})
 
 
