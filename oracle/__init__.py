@@ -95,6 +95,9 @@ def lib():
                                      ctypes.c_int64, P, P, P, P, ctypes.c_int, ctypes.c_uint32,
                                      P, P]
         L.orc_step_quant.restype = ctypes.c_int
+        L.orc_step_fp32m.argtypes = [P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, P, P, P, ctypes.c_uint32, P, P]
+        L.orc_step_fp32m.restype = ctypes.c_int
         L.orc_encode_init.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int, P, P, P, P]
         L.orc_encode_init.restype = ctypes.c_int
@@ -184,7 +187,8 @@ def is_quantized(numel: int, norm: bool) -> bool:
 
 @dataclass
 class State:
-    """Oracle-side optimizer state of one tensor: packed codes + block scales, or FP32 m/v."""
+    """Oracle-side optimizer state of one tensor: packed codes + block scales, or FP32 m/v.
+    A quantized state with mcodes None keeps m in FP32 (m) and only v packed (fp32_m)."""
     quantized: bool
     mcodes: np.ndarray | None = None
     vcodes: np.ndarray | None = None
@@ -193,19 +197,28 @@ class State:
     m: np.ndarray | None = None
     v: np.ndarray | None = None
 
+    @property
+    def fp32_m(self) -> bool:
+        return self.quantized and self.mcodes is None
+
     def copy(self) -> "State":
         c = lambda a: None if a is None else a.copy()
         return State(self.quantized, c(self.mcodes), c(self.vcodes), c(self.mscale),
                      c(self.vscale), c(self.m), c(self.v))
 
 
-def init_state(n: int, norm: bool, mode: int, m0=None, v0=None) -> State:
-    """Zero state, or deterministic RTN encoding of given FP32 moments (ZE-EDEN adds its rescale)."""
+def init_state(n: int, norm: bool, mode: int, m0=None, v0=None, fp32_m: bool = False) -> State:
+    """Zero state, or deterministic RTN encoding of given FP32 moments (ZE-EDEN adds its rescale).
+    fp32_m: a quantized tensor keeps m in FP32 (only v is encoded)."""
     if not is_quantized(n, norm):
         m = np.zeros(n, np.float32) if m0 is None else np.asarray(m0, np.float32).copy()
         v = np.zeros(n, np.float32) if v0 is None else np.asarray(v0, np.float32).copy()
         return State(False, m=m, v=v)
     nb = (n + BLOCK - 1) // BLOCK
+    if fp32_m:
+        full = init_state(n, norm, mode, None, v0)
+        m = np.zeros(n, np.float32) if m0 is None else np.asarray(m0, np.float32).copy()
+        return State(True, None, full.vcodes, None, full.vscale, m=m)
     st = State(True, np.zeros((n + 1) // 2, np.uint8), np.zeros((n + 1) // 2, np.uint8),
                np.zeros(nb, np.float32), np.zeros(nb, np.float32))
     if m0 is not None or v0 is not None:
@@ -225,6 +238,12 @@ def decode(st: State, n: int, mode: int):
         return st.m.copy(), st.v.copy()
     m = np.zeros(n, np.float32)
     v = np.zeros(n, np.float32)
+    if st.fp32_m:
+        dummy_c = np.zeros_like(st.vcodes)
+        dummy_s = np.zeros_like(st.vscale)
+        lib().orc_decode(_p(dummy_c), _p(st.vcodes), _p(dummy_s), _p(st.vscale), n, mode,
+                         _p(m), _p(v))
+        return st.m.copy(), v
     lib().orc_decode(_p(st.mcodes), _p(st.vcodes), _p(st.mscale), _p(st.vscale), n, mode,
                      _p(m), _p(v))
     return m, v
@@ -252,6 +271,12 @@ def step_tensor(w: np.ndarray, g: np.ndarray, st: State, hp: HParams, *, pos: in
     n = cnt if n is None else n
     d = np.full((cnt, 4), -1.0, np.float32) if dbg else None
     h = hp.c()
+    if st.fp32_m:
+        rc = lib().orc_step_fp32m(_p(w), _p(ga), bf16, n, e0, cnt, _p(st.m), _p(st.vcodes),
+                                  _p(st.vscale), pos, ctypes.byref(h), _p(d))
+        if rc != 0:
+            raise ValueError("bad element range or mode for the oracle step")
+        return d
     rc = lib().orc_step_quant(_p(w), _p(ga), bf16, n, e0, cnt, _p(st.mcodes), _p(st.vcodes),
                               _p(st.mscale), _p(st.vscale), int(head), pos, ctypes.byref(h),
                               _p(d))

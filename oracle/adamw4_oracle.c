@@ -464,6 +464,21 @@ void orc_step_fp32(float* w, const void* g, int g_bf16, int64_t cnt, float* m, f
     }
 }
 
+/* v of one block by the encoder of hp->mode (v decoded with the previous step's codebook). */
+static void encode_v_by_mode(const float* vw, int nvalid, const orc_hparams* hp,
+                             const orc_scalars_t* s, const float V0[16], const float V1[16],
+                             uint32_t pos, int64_t i0, uint8_t* cv, float* vscale, orc_dbg* d) {
+    switch (hp->mode) {
+    case ORC_ZIP_SR:
+        encode_v_zip_block(vw, nvalid, V0, s->rs2, hp->eps, hp->seed, hp->step, pos, i0, cv, vscale, d);
+        break;
+    case ORC_ZE_EDEN: encode_v_eden_block(vw, V1, cv, vscale); break;
+    case ORC_V_RTN: encode_v_rtn_block(vw, V0, cv, vscale); break;
+    case ORC_V_SSR: encode_v_ssr_block(vw, nvalid, V0, hp->seed, hp->step, pos, i0, cv, vscale, d); break;
+    default: encode_v_prtn_block(vw, nvalid, V0, s->rs2, hp->eps, cv, vscale, d); break;
+    }
+}
+
 /* Quantized tensor of n elements; this call covers elements [e0, e0 + cnt), e0 a multiple of
  * 128.  Every array points at the data for element e0: w[0], g[0], codes byte e0/2, scale
  * e0/128.  pos is the tensor's position in the step's tensor list (RNG key), is_head marks the
@@ -504,21 +519,54 @@ int orc_step_quant(float* w, const void* g, int g_bf16, int64_t n, int64_t e0, i
             }
             orc_dbg* d = dbg ? dbg + lo : NULL;
             encode_m_block(mw, nvalid, sr_m, NF4, hp->seed, hp->step, pos, e0 + lo, cm, &mscale[b], d);
-            switch (hp->mode) {
-            case ORC_ZIP_SR:
-                encode_v_zip_block(vw, nvalid, V0, s.rs2, hp->eps, hp->seed, hp->step, pos, e0 + lo,
-                                   cv, &vscale[b], d);
-                break;
-            case ORC_ZE_EDEN: encode_v_eden_block(vw, V1, cv, &vscale[b]); break;
-            case ORC_V_RTN: encode_v_rtn_block(vw, V0, cv, &vscale[b]); break;
-            case ORC_V_SSR:
-                encode_v_ssr_block(vw, nvalid, V0, hp->seed, hp->step, pos, e0 + lo, cv, &vscale[b], d);
-                break;
-            default:
-                encode_v_prtn_block(vw, nvalid, V0, s.rs2, hp->eps, cv, &vscale[b], d);
-                break;
-            }
+            encode_v_by_mode(vw, nvalid, hp, &s, V0, V1, pos, e0 + lo, cv, &vscale[b], d);
             pack_block(cm, nvalid, mcodes + lo / 2);
+            pack_block(cv, nvalid, vcodes + lo / 2);
+        }
+    }
+    return 0;
+}
+
+/* A quantized tensor whose first moment stays in FP32 (the controlled study's configuration,
+ * [lav-RO]: FP32 first moments, 4-bit v on the zero-inclusive codebook): m32 holds the cnt FP32
+ * first moments for elements [e0, e0 + cnt) and is updated in place; v is decoded, updated and
+ * encoded exactly as in orc_step_quant.  Returns 0, or -1 on a bad range or mode. */
+int orc_step_fp32m(float* w, const void* g, int g_bf16, int64_t n, int64_t e0, int64_t cnt,
+                   float* m32, uint8_t* vcodes, float* vscale, uint32_t pos,
+                   const orc_hparams* hp, float* dbg_out) {
+    if (e0 < 0 || cnt < 0 || (e0 % ORC_BLOCK) != 0 || e0 + cnt > n) return -1;
+    if (hp->mode < ORC_ZIP_SR || hp->mode > ORC_V_PRTN) return -1;
+    if (cnt == 0) return 0;
+    float V0[16], V1[16];
+    v0_table(V0); v1_table(V1);
+    const float* Vprev = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZE_EDEN) ? V1 : V0;
+    orc_scalars_t s = scalars_of(hp);
+    int64_t nblk = (cnt + ORC_BLOCK - 1) / ORC_BLOCK;
+    orc_dbg* dbg = (orc_dbg*)dbg_out;
+
+#pragma omp parallel
+    {
+        ieee_mode();
+#pragma omp for schedule(static)
+        for (int64_t b = 0; b < nblk; ++b) {
+            int64_t lo = b * ORC_BLOCK;
+            int nvalid = (int)((cnt - lo) < ORC_BLOCK ? (cnt - lo) : ORC_BLOCK);
+            float vnew[ORC_BLOCK];
+            uint8_t cv[ORC_BLOCK];
+            float sv_old = vscale[b];
+            for (int j = 0; j < ORC_BLOCK; ++j) {
+                if (j >= nvalid) { vnew[j] = 0.0f; continue; }
+                int64_t i = lo + j;
+                float v_old = Vprev[unpack(vcodes + lo / 2, j)] * sv_old;
+                orc_elem e = adamw_elem(w[i], widen_grad(g, g_bf16, i), m32[i], v_old, hp, &s);
+                w[i] = e.w;
+                m32[i] = e.m;
+                vnew[j] = e.v;
+            }
+            if (dbg)
+                for (int j = 0; j < nvalid; ++j) { dbg[lo + j].u_m = -1.0f; dbg[lo + j].p_m = -1.0f; }
+            encode_v_by_mode(vnew, nvalid, hp, &s, V0, V1, pos, e0 + lo, cv, &vscale[b],
+                             dbg ? dbg + lo : NULL);
             pack_block(cv, nvalid, vcodes + lo / 2);
         }
     }

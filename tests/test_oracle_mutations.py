@@ -46,6 +46,7 @@ MUTANTS = {
                          "float p = (hi - y) / (hi - lo);\n        if (dbg && j < nvalid) { dbg[j].u_v = 0.5f;"),
     "prtn_threshold": ("codes[j] = (uint8_t)(p >= 0.5f ? k : k + 1);",
                        "codes[j] = (uint8_t)(p >= 0.25f ? k : k + 1);"),
+    "fp32m_m_not_updated": ("                m32[i] = e.m;\n", "                m32[i] = m32[i];\n"),
 }
 
 

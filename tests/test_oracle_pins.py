@@ -352,6 +352,37 @@ def test_prtn_is_nearest_in_preconditioner_space(orc):
     assert np.all(codes[1:] == 1) and np.all(dbg[1:, 0] == 0.5)
 
 
+@pytest.mark.parametrize("mode", [0, 2, 3, 4])
+def test_fp32_m_variant(orc, mode):
+    """The controlled study's configuration ([lav-RO]: FP32 first moments, zero-inclusive v):
+    over several steps m equals the FP32 AdamW recurrence bit for bit, v's codes and scales equal
+    those of the fully quantized path from the same v state (the v side never reads m), and the
+    weights equal FP32 AdamW applied to (m, decode(v))."""
+    rng = np.random.default_rng(50 + mode)
+    n = 4096 * 2 + 300
+    w = rng.normal(0, 0.02, n).astype(f32)
+    st = orc.init_state(n, False, mode, fp32_m=True)
+    fp = orc.init_state(n, True, mode)            # FP32 reference for m
+    wq = w.copy()
+    q = orc.init_state(n, False, mode)            # fully quantized path, for v
+    for t in range(1, 6):
+        g = rng.normal(0, 1e-3, n).astype(f32)
+        hp = orc.HParams(step=t, mode=mode, seed=9)
+        m_dec, v_dec = orc.decode(st, n, mode)
+        w_ref = w.copy()
+        orc.step_tensor(w_ref, g, orc.State(False, m=m_dec, v=v_dec), hp, pos=2)
+        q.vcodes[:], q.vscale[:] = st.vcodes, st.vscale
+        orc.step_tensor(wq, g, q, hp, pos=2)
+        orc.step_tensor(w, g, st, hp, pos=2)
+        w_fp = w_ref.copy()
+        orc.step_tensor(w_fp, g, fp, hp, pos=2)
+        assert np.array_equal(st.m.view(np.uint32), fp.m.view(np.uint32))
+        assert np.array_equal(st.vcodes, q.vcodes) and np.array_equal(st.vscale, q.vscale)
+        assert np.array_equal(w.view(np.uint32), w_ref.view(np.uint32))
+        fp.m[:] = st.m
+        fp.v[:] = orc.decode(st, n, mode)[1]
+
+
 def test_closed_form_zero_cell(orc):
     """For a = 0: p = eps (1 - sqrt(v/b)) / (sqrt(v/bc2) + eps) (the worked example's formula with
     bias correction restored per [daiwk-CE])."""
