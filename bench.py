@@ -53,16 +53,19 @@ def kernel_hash() -> str:
 def algorithmic_bytes(w) -> tuple[int, int, int]:
     """(bytes per launch, quantized values, FP32-state values)."""
     gb = 2 if w.grad_dtype == "bf16" else 4
-    q = f = 0
+    q = f = total = 0
     for s in w.specs:
-        if s.numel >= 4096 and not (s.flags & 1):
-            q += s.numel
+        n, nblk = s.numel, (s.numel + 127) // 128
+        if n >= 4096 and not (s.flags & 1):
+            q += n
+            if s.flags & 4:   # FP32 m: w r/w, grad, m r/w, v codes r/w, 2 v-scale words per block
+                total += n * (8 + gb + 8 + 1) + nblk * 8
+            else:             # w r/w, grad, m and v codes r/w, 4 scale words per block
+                total += n * (8 + gb + 2) + nblk * 16
         else:
-            f += s.numel
-    nblk = sum((s.numel + 127) // 128 for s in w.specs if s.numel >= 4096 and not (s.flags & 1))
-    qbytes = q * (8 + gb + 2) + nblk * 16     # w r/w, grad, codes r/w, 4 scale words per block
-    fbytes = f * (8 + gb + 16)                # w r/w, grad, FP32 m and v r/w
-    return qbytes + fbytes, q, f
+            f += n
+            total += n * (8 + gb + 16)   # w r/w, grad, FP32 m and v r/w
+    return total, q, f
 
 
 def pct(xs, p):

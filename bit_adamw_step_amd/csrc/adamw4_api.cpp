@@ -35,6 +35,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Section offsets and total size of one tensor's state.
 size_t layout(int64_t n, uint32_t flags, size_t off[4]) {
+    if (quantized(n, flags) && (flags & ADAMW4_T_FP32_M)) {
+        const size_t m32 = align16(size_t(n) * 4);
+        const size_t codes = align16(size_t((n + 1) / 2));
+        const size_t scales = align16(size_t((n + kBlock - 1) / kBlock) * 4);
+        off[0] = 0;
+        off[1] = m32;
+        off[2] = kNoOffset;
+        off[3] = m32 + codes;
+        return m32 + codes + scales;
+    }
     if (quantized(n, flags)) {
         const size_t codes = align16(size_t((n + 1) / 2));
         const size_t scales = align16(size_t((n + kBlock - 1) / kBlock) * 4);
@@ -55,7 +65,7 @@ size_t layout(int64_t n, uint32_t flags, size_t off[4]) {
 adamw4_status check_tensor_common(const adamw4_tensor& t) {
     if (t.numel < 1) return ADAMW4_EINVAL;
     if (t.numel > ADAMW4_MAX_NUMEL) return ADAMW4_ESIZE;
-    if (t.flags & ~uint32_t(ADAMW4_T_NORM | ADAMW4_T_HEAD)) return ADAMW4_EINVAL;
+    if (t.flags & ~uint32_t(ADAMW4_T_NORM | ADAMW4_T_HEAD | ADAMW4_T_FP32_M)) return ADAMW4_EINVAL;
     if (!t.state) return ADAMW4_EINVAL;
     if (!aligned16(t.state)) return ADAMW4_EALIGN;
     size_t off[4];
@@ -125,10 +135,11 @@ TensorDesc make_desc(const adamw4_tensor& t, uint32_t pos) {
     if (quantized(t.numel, t.flags)) d.flags |= D_QUANT;
     if (t.flags & ADAMW4_T_HEAD) d.flags |= D_HEAD;
     if (t.grad_dtype == ADAMW4_GRAD_BF16) d.flags |= D_BF16;
+    if ((d.flags & D_QUANT) && (t.flags & ADAMW4_T_FP32_M)) d.flags |= D_FP32M;
     d.s0 = base + off[0];
     d.s1 = base + off[1];
     if (d.flags & D_QUANT) {
-        d.s2 = reinterpret_cast<float*>(base + off[2]);
+        d.s2 = (d.flags & D_FP32M) ? nullptr : reinterpret_cast<float*>(base + off[2]);
         d.s3 = reinterpret_cast<float*>(base + off[3]);
     }
     return d;

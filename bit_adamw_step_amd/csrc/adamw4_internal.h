@@ -15,10 +15,11 @@ constexpr int kRows = kWG / kLanes;      // blocks processed per workgroup itera
 constexpr int kMinQuant = 4096;          // smaller tensors keep FP32 moments
 
 // descriptor flags
-enum : uint32_t { D_QUANT = 1u, D_HEAD = 2u, D_BF16 = 4u };
+enum : uint32_t { D_QUANT = 1u, D_HEAD = 2u, D_BF16 = 4u, D_FP32M = 8u };
 
 // One tensor of a launch.  For quantized tensors s0/s1 are the packed m/v codes and s2/s3 the
-// m/v block scales; for FP32 tensors s0/s1 are the FP32 m/v arrays.  aux0/aux1 carry the
+// m/v block scales (with D_FP32M: s0 is the FP32 m array and s2 is unused); for FP32 tensors
+// s0/s1 are the FP32 m/v arrays.  aux0/aux1 carry the
 // initial moments (init) or the decode outputs (decode); unused by the step.
 struct alignas(16) TensorDesc {
     float* param;

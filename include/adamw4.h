@@ -64,8 +64,11 @@ typedef enum {
 
 /* per-tensor flags */
 enum {
-    ADAMW4_T_NORM = 1u, /* normalization-layer tensor: m and v stay FP32 ([lav-ST]) */
-    ADAMW4_T_HEAD = 2u  /* LM-head tensor: its m is rounded stochastically when sr_head is set ([lav-ZE]) */
+    ADAMW4_T_NORM = 1u,  /* normalization-layer tensor: m and v stay FP32 ([lav-ST]) */
+    ADAMW4_T_HEAD = 2u,  /* LM-head tensor: its m is rounded stochastically when sr_head is set ([lav-ZE]) */
+    ADAMW4_T_FP32_M = 4u /* a quantized tensor keeps m in FP32 and only v in 4 bits: the pages'
+                            controlled study of v rounding rules ([lav-RO]); no effect on tensors
+                            that keep both moments in FP32 */
 };
 
 enum { ADAMW4_GRAD_F32 = 0, ADAMW4_GRAD_BF16 = 1 };
@@ -108,12 +111,14 @@ typedef struct {
  * function, no device needed.  Quantized tensors (numel >= 4096 and not NORM): m codes and v
  * codes (ceil(numel/2) bytes each, two 4-bit codes per byte, element 2q in the low nibble of
  * byte q), then m scales and v scales (ceil(numel/128) FP32 each); each section starts on a
- * 16-byte boundary.  Other tensors: FP32 m then FP32 v (numel each, 16-byte aligned sections).
- * Returns 0 when numel is outside 1..ADAMW4_MAX_NUMEL. */
+ * 16-byte boundary.  With ADAMW4_T_FP32_M: FP32 m (numel), v codes, v scales.  Other tensors:
+ * FP32 m then FP32 v (numel each, 16-byte aligned sections).  Returns 0 when numel is outside
+ * 1..ADAMW4_MAX_NUMEL. */
 size_t adamw4_state_bytes(int64_t numel, uint32_t flags);
 
 /* Byte offsets of the state's sections (see adamw4_state_bytes): quantized tensors get
- * {m codes, v codes, m scales, v scales}; FP32 tensors get {m, v, SIZE_MAX, SIZE_MAX}.
+ * {m codes, v codes, m scales, v scales} ({FP32 m, v codes, SIZE_MAX, v scales} with
+ * ADAMW4_T_FP32_M); FP32 tensors get {m, v, SIZE_MAX, SIZE_MAX}.
  * offsets: host, 4 entries.  Returns ADAMW4_EINVAL on a bad numel or null pointer. */
 adamw4_status adamw4_state_layout(int64_t numel, uint32_t flags, size_t offsets[4]);
 

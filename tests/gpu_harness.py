@@ -38,6 +38,10 @@ def oracle_state(buf: np.ndarray, n: int, flags: int, b0: int = 0, nb: int | Non
         nb = nbt - b0 if nb is None else nb
         c0, c1 = 64 * b0, min((n + 1) // 2, 64 * (b0 + nb))
         sc = lambda o: buf[o + 4 * b0: o + 4 * (b0 + nb)].view(f32).copy()
+        if flags & A.T_FP32_M:
+            e0, e1 = 128 * b0, min(n, 128 * (b0 + nb))
+            return orc.State(True, None, buf[off[1] + c0: off[1] + c1].copy(), None, sc(off[3]),
+                             m=buf[off[0] + 4 * e0: off[0] + 4 * e1].view(f32).copy())
         return orc.State(True, buf[off[0] + c0: off[0] + c1].copy(), buf[off[1] + c0: off[1] + c1].copy(),
                          sc(off[2]), sc(off[3]))
     return orc.State(False, m=buf[off[0]: off[0] + 4 * n].view(f32).copy(),
@@ -69,7 +73,15 @@ def compare_state(name: str, n: int, gpu: orc.State, ref: orc.State, dbg: np.nda
                     raise Mismatch(f"{name}: FP32 {k} differs at {np.nonzero(bad)[0][:8]}")
         return
     cnt = n
-    for k, col_u, col_p in (("mcodes", 2, 3), ("vcodes", 0, 1)):
+    packed = (("vcodes", 0, 1),) if ref.fp32_m else (("mcodes", 2, 3), ("vcodes", 0, 1))
+    if ref.fp32_m:
+        exact = np.array_equal(gpu.m.view(np.uint32), ref.m.view(np.uint32))
+        report[f"{name}.m_bitexact"] = exact
+        if not exact:
+            bad = np.abs(gpu.m.astype(np.float64) - ref.m) > 1e-6 * np.abs(ref.m.astype(np.float64)) + 1e-30
+            if bad.any():
+                raise Mismatch(f"{name}: FP32 m differs at {np.nonzero(bad)[0][:8]}")
+    for k, col_u, col_p in packed:
         a, b = unpack(getattr(gpu, k), cnt), unpack(getattr(ref, k), cnt)
         diff = np.nonzero(a != b)[0]
         report[f"{name}.{k}_flips"] = int(diff.size)
@@ -85,7 +97,7 @@ def compare_state(name: str, n: int, gpu: orc.State, ref: orc.State, dbg: np.nda
                                f"oracle {b[j]} u {dbg[j, col_u]} p {dbg[j, col_p]}")
         if cnt % 2 == 1:
             assert getattr(gpu, k)[-1] >> 4 == 0, f"{name}: {k} padding nibble not zero"
-    for k in ("mscale", "vscale"):
+    for k in (("vscale",) if ref.fp32_m else ("mscale", "vscale")):
         a, b = getattr(gpu, k), getattr(ref, k)
         if not np.array_equal(a.view(np.uint32), b.view(np.uint32)):
             j = np.nonzero(a.view(np.uint32) != b.view(np.uint32))[0][:8]

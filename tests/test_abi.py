@@ -43,6 +43,20 @@ def test_exports_every_declared_function(A):
         assert re.search(r"\bT " + n + r"\b", out), n
 
 
+def test_state_bytes_fp32_m(A):
+    """FP32-m tensors: FP32 m, then v codes, then v scales, 16-byte aligned; no m scales."""
+    for n in (4096, 4097, 12345, 1 << 20):
+        off = A.state_layout(n, A.T_FP32_M)
+        m32 = (4 * n + 15) // 16 * 16
+        codes = ((n + 1) // 2 + 15) // 16 * 16
+        scales = ((n + 127) // 128 * 4 + 15) // 16 * 16
+        assert off[0] == 0 and off[1] == m32 and off[2] >= 2**63 and off[3] == m32 + codes
+        assert A.state_bytes(n, A.T_FP32_M) == m32 + codes + scales
+    # tensors that keep both moments in FP32 are unaffected by the flag
+    assert A.state_bytes(100, A.T_FP32_M) == A.state_bytes(100, 0)
+    assert A.state_bytes(5000, A.T_FP32_M | A.T_NORM) == A.state_bytes(5000, A.T_NORM)
+
+
 def test_state_bytes_formula(A):
     """Quantized: two code sections of ceil(n/2) bytes and two scale sections of ceil(n/128)
     FP32, 16-byte aligned; FP32 tensors: 2 x 4n bytes."""

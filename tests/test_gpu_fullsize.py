@@ -5,8 +5,9 @@ tensor are replayed on the oracle from a snapshot taken just before the step.
 
 Lists (workloads module): GPT 130M-shape (ZIP-SR, BF16 row-scaled grads), GPT 834M-shape
 (ZE-EDEN, v pre-seeded 10^U(-20,-4) through the init encoder), Llama 2.7B-shape (ZIP-SR,
-LM-head stochastic rounding switched on at t = 181 of 200), and the stress list (one 2^30-value
-tensor + 2000 FP32-state tensors, Student-t grads with 30% zeros, ZIP-SR / ZE-EDEN alternating).
+LM-head stochastic rounding switched on at t = 181 of 200), the stress list (one 2^30-value
+tensor + 2000 FP32-state tensors, Student-t grads with 30% zeros, ZIP-SR / ZE-EDEN alternating),
+and the 834M shapes with FP32 first moments under the four zero-inclusive v rules in turn.
 """
 import numpy as np
 import pytest
@@ -73,9 +74,14 @@ def _grab(pl, A, w, i, e0, cnt):
         b0, nb = e0 // 128, (cnt + 127) // 128
         c0, c1 = e0 // 2, (e0 + cnt + 1) // 2
         sl = lambda o, a, z: to_np(buf[o + a:o + z]).copy()
-        st = orc.State(True, sl(off[0], c0, c1), sl(off[1], c0, c1),
-                       sl(off[2], 4 * b0, 4 * (b0 + nb)).view(np.float32),
-                       sl(off[3], 4 * b0, 4 * (b0 + nb)).view(np.float32))
+        if s.flags & A.T_FP32_M:
+            st = orc.State(True, None, sl(off[1], c0, c1), None,
+                           sl(off[3], 4 * b0, 4 * (b0 + nb)).view(np.float32),
+                           m=sl(off[0], 4 * e0, 4 * (e0 + cnt)).view(np.float32))
+        else:
+            st = orc.State(True, sl(off[0], c0, c1), sl(off[1], c0, c1),
+                           sl(off[2], 4 * b0, 4 * (b0 + nb)).view(np.float32),
+                           sl(off[3], 4 * b0, 4 * (b0 + nb)).view(np.float32))
     else:
         st = orc.State(False, m=to_np(buf[off[0]:off[0] + 4 * n]).view(np.float32).copy(),
                        v=to_np(buf[off[1]:off[1] + 4 * n]).view(np.float32).copy())
@@ -151,3 +157,10 @@ def test_gpt834m_full(env):
 @pytest.mark.timeout(900)
 def test_stress_full(env):
     _run(env, "stress", {1, 2, 3, 20})
+
+
+@pytest.mark.timeout(900)
+def test_study834m_full(env):
+    """834M GPT shapes with FP32 first moments, v by ZIP-SR / state RTN / state SR /
+    preconditioner RTN in turn (the controlled study's configuration)."""
+    _run(env, "study834m", {1, 2, 3, 4, 5, 40})

@@ -53,8 +53,8 @@ def test_init_matches_oracle(env, mode):
     import torch
     from gpu_harness import GpuList, oracle_state, compare_state, say
     A, orc = env
-    sizes = [4096, 4097, 128 * 37 + 5, 9000, 100, 6000]
-    flags = [0, 0, A.T_HEAD, 0, 0, A.T_NORM]
+    sizes = [4096, 4097, 128 * 37 + 5, 9000, 100, 6000, 128 * 33 + 9]
+    flags = [0, 0, A.T_HEAD, 0, 0, A.T_NORM, A.T_FP32_M]
     gl = GpuList(sizes, flags, ["f32"] * len(sizes))
     rng = np.random.default_rng(mode)
     m0, v0 = [], []
@@ -73,7 +73,8 @@ def test_init_matches_oracle(env, mode):
     _, _, ss = gl.snapshot()
     rep = {}
     for i, n in enumerate(sizes):
-        ref = orc.init_state(n, bool(flags[i] & A.T_NORM), mode, m0[i], None if i == 1 else v0[i])
+        ref = orc.init_state(n, bool(flags[i] & A.T_NORM), mode, m0[i], None if i == 1 else v0[i],
+                             fp32_m=bool(flags[i] & A.T_FP32_M))
         compare_state(f"init{i}", n, oracle_state(ss[i], n, flags[i]), ref, None, rep)
 
 
@@ -82,8 +83,9 @@ def test_decode_matches_oracle(env, mode):
     import torch
     from gpu_harness import GpuList, to_np, say
     A, orc = env
-    sizes = [4096 * 2 + 77, 300]
-    gl = GpuList(sizes, [0, 0], ["f32", "f32"])
+    sizes = [4096 * 2 + 77, 300, 4096 + 129]
+    fl = [0, 0, A.T_FP32_M]
+    gl = GpuList(sizes, fl, ["f32"] * 3)
     rng = np.random.default_rng(3)
     m0 = [rng.normal(0, 1, n).astype(f32) for n in sizes]
     v0 = [rng.random(n).astype(f32) for n in sizes]
@@ -93,7 +95,7 @@ def test_decode_matches_oracle(env, mode):
         vo = torch.empty(n, device="cuda")
         say(f"decode tensor {i} n={n} mode={mode}")
         A.decode_state(gl.pl.array[i], mode, mo.data_ptr(), vo.data_ptr())
-        ref = orc.init_state(n, False, mode, m0[i], v0[i])
+        ref = orc.init_state(n, False, mode, m0[i], v0[i], fp32_m=bool(fl[i] & A.T_FP32_M))
         rm, rv = orc.decode(ref, n, mode)
         assert np.array_equal(to_np(mo), rm) and np.array_equal(to_np(vo), rv)
 
@@ -149,6 +151,20 @@ def test_study_modes(env):
              (7, A.ZE_EDEN, P, 0), (8, S, A.ZE_EDEN, 1), (9, A.ZIP_SR, S, 0), (10, R, A.ZIP_SR, 0)]
     rep = _run_steps(env, sizes, flags, gdt, sched, seed=8)
     print({k: v for k, v in rep.items() if "flips" in k and v})
+
+
+def test_fp32_m_tensors(env):
+    """Quantized tensors that keep m in FP32 (the controlled study's configuration) next to
+    ordinary ones, ragged lengths, head and norm flags, BF16 and FP32 grads, every v mode."""
+    A = env[0]
+    F = A.T_FP32_M
+    sizes = [4096, 4097, 128 * 50 + 3, 5000, 128 * 200, 33333, 300]
+    flags = [F, F, F, F | A.T_NORM, F | A.T_HEAD, 0, F]
+    gdt = ["f32", "bf16", "bf16", "f32", "bf16", "f32", "bf16"]
+    sched = [(1, A.ZIP_SR, -1, 0), (2, A.V_SSR, A.ZIP_SR, 1), (3, A.V_RTN, A.V_SSR, 0),
+             (4, A.V_PRTN, A.V_RTN, 1), (5, A.ZE_EDEN, A.V_PRTN, 0), (6, A.ZIP_SR, A.ZE_EDEN, 1)]
+    rep = _run_steps(env, sizes, flags, gdt, sched, seed=10)
+    assert all(v for k, v in rep.items() if k.endswith("m_bitexact"))
 
 
 def test_edge_cases(env):

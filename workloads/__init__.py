@@ -13,6 +13,9 @@ Llama-style models of 130M-2.7B parameters, zhichai.net summary and kongchang.co
           BF16 grads N(0, 1e-3)
   stress  one 2^30-value FP32 tensor + 2000 tensors of U{64..4095} values (FP32 states);
           FP32 grads 1e-3 * Student-t(3) with 30% exact zeros
+  study834m the 834M GPT shapes with FP32 first moments on the quantized tensors and the
+          zero-inclusive v rules in turn (ZIP-SR, state RTN, state SR, preconditioner RTN), the
+          configuration of the pages' controlled study (learnaivisually.com explainer)
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-T_NORM, T_HEAD = 1, 2
+T_NORM, T_HEAD, T_FP32_M = 1, 2, 4
 
 
 @dataclass(frozen=True)
@@ -62,6 +65,12 @@ def llama_list(d: int, layers: int, hidden: int, vocab: int) -> list[PSpec]:
     return L
 
 
+def with_fp32_m(specs) -> list[PSpec]:
+    """The same list with the first moment kept in FP32 on every non-norm tensor."""
+    return [s if s.flags & T_NORM else PSpec(s.name, s.shape, s.flags | T_FP32_M, s.init)
+            for s in specs]
+
+
 def stress_list(seed: int = 5) -> list[PSpec]:
     rng = np.random.default_rng(seed)
     sizes = rng.integers(64, 4096, 2000)
@@ -73,7 +82,7 @@ class Workload:
     name: str
     specs: tuple
     grad_dtype: str          # "f32" | "bf16"
-    mode_schedule: str       # "zip" | "eden" | "alternate"
+    mode_schedule: str       # "zip" | "eden" | "alternate" | "study"
     steps: int
     data_seed: int
     grad_kind: str = "normal"   # normal | rowscaled | student_t
@@ -89,6 +98,8 @@ class Workload:
             return 0
         if self.mode_schedule == "eden":
             return 1
+        if self.mode_schedule == "study":   # ZIP-SR, state RTN, state SR, preconditioner RTN
+            return (0, 2, 3, 4)[t % 4]
         return 0 if t % 2 == 1 else 1
 
     def sr_head_at(self, t: int) -> int:
@@ -106,6 +117,8 @@ WORKLOADS = {
                          1004),
     "stress": Workload("stress", tuple(stress_list()), "f32", "alternate", 20, 1005,
                        grad_kind="student_t"),
+    "study834m": Workload("study834m", tuple(with_fp32_m(gpt_list(1536, 24, 50304))), "bf16", "study",
+                          40, 1006),
 }
 
 
