@@ -26,9 +26,18 @@ _LIB_OVERRIDE = os.environ.get("ADAMW4_ORACLE_LIB")
 
 BLOCK = 128          # values per FP32 block scale ([lav-ST])
 MIN_QUANT = 4096     # tensors below this stay FP32 ([daiwk-LR])
-ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN = 0, 1, 2, 3, 4
+# v encoders: the two methods, the controlled study's three other rules, and the baseline
+# (round to nearest on the zero-free codebook, absmax scale, no rescale)
+ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN, V_ZE_RTN = 0, 1, 2, 3, 4, 5
+MODES = (ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN, V_ZE_RTN)
 CB_NF4, CB_V0, CB_V1 = 0, 1, 2
-RULE_M_RTN, RULE_M_SR, RULE_V_ZIP, RULE_V_EDEN, RULE_V_RTN, RULE_V_SSR, RULE_V_PRTN = 0, 1, 2, 3, 4, 5, 6
+(RULE_M_RTN, RULE_M_SR, RULE_V_ZIP, RULE_V_EDEN, RULE_V_RTN, RULE_V_SSR, RULE_V_PRTN,
+ RULE_V_ZE_RTN) = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def v_codebook_of(mode: int) -> int:
+    """Codebook a v encoded under `mode` decodes with: V1 for ZE-EDEN and the baseline."""
+    return CB_V1 if mode in (ZE_EDEN, V_ZE_RTN) else CB_V0
 
 
 def build(force: bool = False) -> str:

@@ -42,6 +42,8 @@
  *   - the controlled study's other v rules ([lav-RO]) on the zero-inclusive codebook:
  *     state-space RTN (nearest level), state-space SR (lower level with probability
  *     (b-y)/(b-a)), preconditioner-space RTN (the level with the nearest h; a tie goes low).
+ *   - the baseline the pages measure against: RTN on the zero-free V1, absmax scale, no rescale
+ *     (ZE-EDEN without its gamma).
  *   - RNG: Philox4x32-10 (Salmon et al., SC'11) keyed by the seed, counter
  *     (j lo, j hi | stream<<31, tensor position, t) with j = i >> 2; u = (word >> 8) * 2^-24;
  *     the lower level is chosen iff u < p.
@@ -56,10 +58,16 @@
 #define ORC_BLOCK 128
 #define ORC_MIN_QUANT 4096
 
-/* v encoders: the two methods, and the controlled study's other rules on the zero-inclusive
+/* v encoders: the two methods, the controlled study's other rules on the zero-inclusive
  * codebook ([lav-RO]: state-space round-to-nearest and stochastic rounding, preconditioner-space
- * round-to-nearest) */
-enum { ORC_ZIP_SR = 0, ORC_ZE_EDEN = 1, ORC_V_RTN = 2, ORC_V_SSR = 3, ORC_V_PRTN = 4 };
+ * round-to-nearest), and the baseline the pages compare against ([lav-ZE], [lav-ST]: the
+ * zero-free codebook with its positive floor, round to nearest, plain absmax scale) */
+enum { ORC_ZIP_SR = 0, ORC_ZE_EDEN = 1, ORC_V_RTN = 2, ORC_V_SSR = 3, ORC_V_PRTN = 4,
+       ORC_V_ZE_RTN = 5 };
+
+/* codebook that a v encoded under `mode` decodes with: the zero-free one for ZE-EDEN and for
+ * the baseline rule (round to nearest on the zero-free codebook, absmax scale, no rescale) */
+static int uses_v1(int mode) { return mode == ORC_ZE_EDEN || mode == ORC_V_ZE_RTN; }
 enum { ORC_CB_NF4 = 0, ORC_CB_V0 = 1, ORC_CB_V1 = 2 };
 
 typedef struct {
@@ -475,6 +483,7 @@ static void encode_v_by_mode(const float* vw, int nvalid, const orc_hparams* hp,
     case ORC_ZE_EDEN: encode_v_eden_block(vw, V1, cv, vscale); break;
     case ORC_V_RTN: encode_v_rtn_block(vw, V0, cv, vscale); break;
     case ORC_V_SSR: encode_v_ssr_block(vw, nvalid, V0, hp->seed, hp->step, pos, i0, cv, vscale, d); break;
+    case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V1, cv, vscale); break;
     default: encode_v_prtn_block(vw, nvalid, V0, s->rs2, hp->eps, cv, vscale, d); break;
     }
 }
@@ -488,12 +497,12 @@ int orc_step_quant(float* w, const void* g, int g_bf16, int64_t n, int64_t e0, i
                    uint8_t* mcodes, uint8_t* vcodes, float* mscale, float* vscale,
                    int is_head, uint32_t pos, const orc_hparams* hp, float* dbg_out) {
     if (e0 < 0 || cnt < 0 || (e0 % ORC_BLOCK) != 0 || e0 + cnt > n) return -1;
-    if (hp->mode < ORC_ZIP_SR || hp->mode > ORC_V_PRTN) return -1;
+    if (hp->mode < ORC_ZIP_SR || hp->mode > ORC_V_ZE_RTN) return -1;
     if (cnt == 0) return 0;
     float NF4[16], V0[16], V1[16];
     nf4_table(NF4); v0_table(V0); v1_table(V1);
-    /* ZE-EDEN's codebook excludes zero; every other encoder uses the zero-inclusive one */
-    const float* Vin = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZE_EDEN) ? V1 : V0;
+    /* ZE-EDEN's and the baseline's codebook excludes zero; the others use the zero-inclusive one */
+    const float* Vin = uses_v1(hp->prev_mode < 0 ? hp->mode : hp->prev_mode) ? V1 : V0;
     orc_scalars_t s = scalars_of(hp);
     int sr_m = (is_head && hp->sr_head) ? 1 : 0;
     int64_t nblk = (cnt + ORC_BLOCK - 1) / ORC_BLOCK;
@@ -535,11 +544,11 @@ int orc_step_fp32m(float* w, const void* g, int g_bf16, int64_t n, int64_t e0, i
                    float* m32, uint8_t* vcodes, float* vscale, uint32_t pos,
                    const orc_hparams* hp, float* dbg_out) {
     if (e0 < 0 || cnt < 0 || (e0 % ORC_BLOCK) != 0 || e0 + cnt > n) return -1;
-    if (hp->mode < ORC_ZIP_SR || hp->mode > ORC_V_PRTN) return -1;
+    if (hp->mode < ORC_ZIP_SR || hp->mode > ORC_V_ZE_RTN) return -1;
     if (cnt == 0) return 0;
     float V0[16], V1[16];
     v0_table(V0); v1_table(V1);
-    const float* Vprev = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZE_EDEN) ? V1 : V0;
+    const float* Vprev = uses_v1(hp->prev_mode < 0 ? hp->mode : hp->prev_mode) ? V1 : V0;
     orc_scalars_t s = scalars_of(hp);
     int64_t nblk = (cnt + ORC_BLOCK - 1) / ORC_BLOCK;
     orc_dbg* dbg = (orc_dbg*)dbg_out;
@@ -593,7 +602,7 @@ int orc_encode_init(const float* m0, const float* v0, int64_t n, int64_t e0, int
         }
         encode_m_block(mw, nvalid, 0, NF4, 0, 0, 0, 0, cm, &mscale[b], NULL);
         if (mode == ORC_ZE_EDEN) encode_v_eden_block(vw, V1, cv, &vscale[b]);
-        else encode_v_rtn_block(vw, V0, cv, &vscale[b]);
+        else encode_v_rtn_block(vw, uses_v1(mode) ? V1 : V0, cv, &vscale[b]);
         pack_block(cm, nvalid, mcodes + lo / 2);
         pack_block(cv, nvalid, vcodes + lo / 2);
     }
@@ -606,7 +615,7 @@ void orc_decode(const uint8_t* mcodes, const uint8_t* vcodes, const float* mscal
                 const float* vscale, int64_t cnt, int mode, float* m_out, float* v_out) {
     float NF4[16], V0[16], V1[16];
     nf4_table(NF4); v0_table(V0); v1_table(V1);
-    const float* V = (mode == ORC_ZE_EDEN) ? V1 : V0;
+    const float* V = uses_v1(mode) ? V1 : V0;
     ieee_mode();
     for (int64_t i = 0; i < cnt; ++i) {
         int64_t b = i / ORC_BLOCK;
@@ -619,7 +628,8 @@ void orc_decode(const uint8_t* mcodes, const uint8_t* vcodes, const float* mscal
 
 /* Block encoders exposed for the pin tests: one 128-slot block (x padded with zeros by the
  * caller), codes unpacked, rule 0 = m RTN, 1 = m SR, 2 = v ZIP-SR, 3 = v ZE-EDEN, 4 = v RTN on
- * V0 (init).  i0 is the global element index of slot 0 (RNG counter). */
+ * V0 (also init), 5 = v state-space SR, 6 = v preconditioner-space RTN, 7 = v RTN on V1 (the
+ * baseline).  i0 is the global element index of slot 0 (RNG counter). */
 void orc_encode_block(const float* x, int nvalid, int rule, float rs2, float eps, uint64_t seed,
                       int64_t t, uint32_t pos, int64_t i0, uint8_t* codes, float* scale,
                       float* dbg_out) {
@@ -634,6 +644,7 @@ void orc_encode_block(const float* x, int nvalid, int rule, float rs2, float eps
     case 3: encode_v_eden_block(x, V1, codes, scale); break;
     case 5: encode_v_ssr_block(x, nvalid, V0, seed, t, pos, i0, codes, scale, d); break;
     case 6: encode_v_prtn_block(x, nvalid, V0, rs2, eps, codes, scale, d); break;
+    case 7: encode_v_rtn_block(x, V1, codes, scale); break;
     default: encode_v_rtn_block(x, V0, codes, scale); break;
     }
 }

@@ -24,7 +24,8 @@ MUTANTS = {
     "zip_sqrt_swapped": ("float n2 = sb + sa;", "float n2 = sb + sy;"),
     "zip_choice_inverted": ("codes[j] = (uint8_t)(u < p ? k : k + 1);\n    }\n}\n\n/* v block under ZE-EDEN",
                             "codes[j] = (uint8_t)(u < p ? k + 1 : k);\n    }\n}\n\n/* v block under ZE-EDEN"),
-    "zip_state_space_p": ("float p = orc_zip_p(y, lo, hi, c, eps);", "float p = (hi - y) / (hi - lo);"),
+    "zip_state_space_p": ("float p = orc_zip_p(y, lo, hi, c, eps);\n        float u = orc_uniform(seed, t, pos, 0, i0 + j);",
+                          "float p = (hi - y) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 0, i0 + j);"),
     "m_sr_p_inverted": ("float p = (hi - y) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 1, i0 + j);",
                         "float p = (y - lo) / (hi - lo);\n        float u = orc_uniform(seed, t, pos, 1, i0 + j);"),
     "rtn_ties_high": ("if (y > mid) ++code;", "if (y >= mid) ++code;"),
@@ -33,8 +34,8 @@ MUTANTS = {
     "eden_no_rescale": ("*scale = gamma * s;", "*scale = s;"),
     "philox_key_bump": ("k1 += 0xBB67AE85u;", "k1 += 0x9E3779B9u;"),
     "rng_stream_ignored": ("(uint32_t)(j >> 32) | ((uint32_t)stream << 31)", "(uint32_t)(j >> 32)"),
-    "prev_mode_ignored": ("const float* Vin = ((hp->prev_mode < 0 ? hp->mode : hp->prev_mode) == ORC_ZIP_SR) ? V0 : V1;",
-                          "const float* Vin = (hp->mode == ORC_ZIP_SR) ? V0 : V1;"),
+    "prev_mode_ignored": ("const float* Vin = uses_v1(hp->prev_mode < 0 ? hp->mode : hp->prev_mode) ? V1 : V0;",
+                          "const float* Vin = uses_v1(hp->mode) ? V1 : V0;"),
     "v0_codebook_k16": ("out[k] = (float)((double)k / 15.0);", "out[k] = (float)((double)k / 16.0);"),
     "nf4_delta": ("const double delta = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);",
                   "const double delta = 0.9677083;"),
@@ -47,6 +48,12 @@ MUTANTS = {
     "prtn_threshold": ("codes[j] = (uint8_t)(p >= 0.5f ? k : k + 1);",
                        "codes[j] = (uint8_t)(p >= 0.25f ? k : k + 1);"),
     "fp32m_m_not_updated": ("                m32[i] = e.m;\n", "                m32[i] = m32[i];\n"),
+    "baseline_keeps_zero": ("case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V1, cv, vscale); break;",
+                            "case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V0, cv, vscale); break;"),
+    "baseline_rescales": ("case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V1, cv, vscale); break;",
+                          "case ORC_V_ZE_RTN: encode_v_eden_block(vw, V1, cv, vscale); break;"),
+    "baseline_decodes_v0": ("static int uses_v1(int mode) { return mode == ORC_ZE_EDEN || mode == ORC_V_ZE_RTN; }",
+                            "static int uses_v1(int mode) { return mode == ORC_ZE_EDEN; }"),
 }
 
 

@@ -174,7 +174,7 @@ def _quant_tensor(orc, n, rng, head=False, mode=0):
     return w, st
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
 def test_step1_weights_equal_fp32_adamw(orc, mode):
     """From m0 = v0 = 0 the quantized state decodes to 0, and weights are updated from the
     unquantized working moments before requantization ([daiwk-CE], [daiwk-PM]), so step-1
@@ -192,7 +192,8 @@ def test_step1_weights_equal_fp32_adamw(orc, mode):
 
 
 @pytest.mark.parametrize("mode,prev", [(0, -1), (1, -1), (1, 0), (0, 1), (2, -1), (3, -1),
-                                       (4, -1), (3, 1), (1, 4), (2, 0)])
+                                       (4, -1), (3, 1), (1, 4), (2, 0), (5, -1), (5, 1),
+                                       (1, 5), (0, 5), (5, 2)])
 def test_every_step_uses_decoded_state(orc, mode, prev):
     """Each step's weights = FP32 AdamW applied to decode(state) (decode -> update -> weights,
     [daiwk-PM] flowchart); the codebook for decoding is the one that encoded the state."""
@@ -352,7 +353,7 @@ def test_prtn_is_nearest_in_preconditioner_space(orc):
     assert np.all(codes[1:] == 1) and np.all(dbg[1:, 0] == 0.5)
 
 
-@pytest.mark.parametrize("mode", [0, 2, 3, 4])
+@pytest.mark.parametrize("mode", [0, 2, 3, 4, 5])
 def test_fp32_m_variant(orc, mode):
     """The controlled study's configuration ([lav-RO]: FP32 first moments, zero-inclusive v):
     over several steps m equals the FP32 AdamW recurrence bit for bit, v's codes and scales equal
@@ -471,7 +472,7 @@ def test_zip_zero_value_and_zero_block(orc):
     codes, s, _ = orc.encode_block(x, orc.RULE_V_ZIP, rs2=1.0)
     assert s == f32(1e-6) and codes[5] == 15 and np.all(np.delete(codes, 5) == 0)
     for rule, zc in [(orc.RULE_M_RTN, 7), (orc.RULE_M_SR, 7), (orc.RULE_V_ZIP, 0),
-                     (orc.RULE_V_EDEN, 0), (orc.RULE_V_RTN, 0)]:
+                     (orc.RULE_V_EDEN, 0), (orc.RULE_V_RTN, 0), (orc.RULE_V_ZE_RTN, 0)]:
         codes, s, _ = orc.encode_block(np.zeros(128, f32), rule)
         assert s == 0.0 and np.all(codes == zc)
 
@@ -581,10 +582,64 @@ def test_eden_no_zero_and_scale_closed_form(orc):
 
 
 # ---------------------------------------------------------------------------------------------
+# P-8b  the baseline: zero-free codebook, round to nearest, absmax scale, no rescale
+# ---------------------------------------------------------------------------------------------
+
+def test_baseline_is_eden_without_rescale(orc):
+    """The baseline keeps the positive floor ([lav-ZE]: TorchAO's; [lav-ST]: the bottom notch
+    is a small positive number), so no value of a non-zero block decodes to zero; it takes the
+    same nearest V1 codes as ZE-EDEN ([kc-TC]: ZE-EDEN = zero removal + block rescale) and
+    stores the plain absmax, which ZE-EDEN multiplies by gamma."""
+    V1 = orc.codebook(orc.CB_V1)
+    rng = np.random.default_rng(41)
+    rescaled = 0
+    for trial in range(200):
+        x = (10 ** rng.uniform(-20, -4, 128)).astype(f32)
+        if trial % 3 == 0:
+            x[rng.random(128) < 0.4] = 0
+        c_b, s_b, _ = orc.encode_block(x, orc.RULE_V_ZE_RTN)
+        c_e, s_e, _ = orc.encode_block(x, orc.RULE_V_EDEN)
+        assert np.array_equal(c_b, c_e)
+        assert s_b == x.max()
+        dec = V1[c_b] * s_b
+        assert np.all(dec >= s_b / 16) and np.all(dec > 0)
+        rescaled += int(s_e != s_b)
+    assert rescaled > 150           # ZE-EDEN's gamma moves the scale; the baseline never does
+
+
+def test_baseline_step_brute_force(orc):
+    """A 3-element tensor (one block) stepped under the baseline, over every incoming v code:
+    incoming v decodes with V1, and the new v codes are the nearest V1 level to v'/max v'
+    (binary64 brute force), scale max v'."""
+    V1 = orc.codebook(orc.CB_V1).astype(np.float64)
+    n = 3
+    hp = orc.HParams(step=6, mode=orc.V_ZE_RTN)
+    for cv in range(16):
+        for g1 in [0.0, 1e-3, -4e-4, 3e-5]:
+            st = orc.State(True, np.array([0x77, 7], np.uint8),
+                           np.array([cv | (3 << 4), 15], np.uint8),
+                           np.array([1e-3], f32), np.array([1e-6], f32))
+            w = np.array([0.01, -0.02, 0.03], f32)
+            g = np.array([g1, -g1, 2e-3], f32)
+            _, v_in = orc.decode(st, n, orc.V_ZE_RTN)
+            assert v_in[0] == f32(V1[cv]) * f32(1e-6) and v_in[1] == f32(V1[3]) * f32(1e-6)
+            orc.step_tensor(w, g, st, hp, pos=0, n=n)
+            b2 = float(f32(hp.beta2))
+            v64 = b2 * v_in.astype(np.float64) + (1 - b2) * g.astype(np.float64) ** 2
+            assert abs(st.vscale[0] - v64.max()) <= 4 * 2**-24 * v64.max()
+            for j in range(n):
+                dd = np.abs(v64[j] / v64.max() - V1)
+                cands = np.nonzero(dd <= dd.min() + 1e-6)[0]
+                code = (st.vcodes[j >> 1] >> (4 * (j & 1))) & 15
+                assert code in cands, (cv, g1, j, code, cands)
+            assert st.vcodes[1] >> 4 == 0
+
+
+# ---------------------------------------------------------------------------------------------
 # P-9 / P-15  round-to-nearest vs brute force; tiny tensors enumerated
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("rule,cb", [(0, 0), (3, 2), (4, 1)])
+@pytest.mark.parametrize("rule,cb", [(0, 0), (3, 2), (4, 1), (7, 2)])
 def test_rtn_is_nearest_level(orc, rule, cb):
     """RTN = argmin over 16 levels |y - C[k]| (binary64); disagreement only where y sits within
     an ulp of a midpoint (the FP32 midpoint decides)."""
@@ -592,8 +647,10 @@ def test_rtn_is_nearest_level(orc, rule, cb):
     rng = np.random.default_rng(12 + rule)
     for _ in range(40):
         x = rng.normal(0, 1, 128).astype(f32) if rule == 0 else rng.random(128).astype(f32) ** 3
-        codes, _, _ = orc.encode_block(x, rule)
+        codes, scale, _ = orc.encode_block(x, rule)
         s = np.abs(x).max()  # codes are chosen on x / absmax (ZE-EDEN stores gamma * absmax)
+        if rule != orc.RULE_V_EDEN:
+            assert scale == s
         y = (x * (f32(1) / f32(s))).astype(np.float64)
         d = np.abs(y[:, None] - C[None, :])
         best = d.argmin(1)
