@@ -98,7 +98,7 @@ def timed_schedule(w, K: int) -> list[int]:
     return [max(1, round((k + 1) * w.steps / K)) for k in range(K)]
 
 
-V_MODES = {"zip": 0, "eden": 1, "rtn": 2, "ssr": 3, "prtn": 4}
+V_MODES = {"zip": 0, "eden": 1, "rtn": 2, "ssr": 3, "prtn": 4, "baseline": 5}
 
 
 def run_gpu(w, steps: int, warmup: int, device, v_mode: str | None = None):

@@ -14,7 +14,7 @@ from dataclasses import dataclass, field
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libadamw4.so")
 
-ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN = 0, 1, 2, 3, 4   # adamw4_mode
+ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN, V_ZE_RTN = 0, 1, 2, 3, 4, 5   # adamw4_mode
 T_NORM, T_HEAD, T_FP32_M = 1, 2, 4
 GRAD_F32, GRAD_BF16 = 0, 1
 CB_NF4, CB_V0, CB_V1 = 0, 1, 2

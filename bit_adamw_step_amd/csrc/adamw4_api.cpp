@@ -84,7 +84,7 @@ adamw4_status check_tensor_step(const adamw4_tensor& t) {
 
 bool finite(float x) { return std::isfinite(x); }
 
-bool valid_mode(int32_t m) { return m >= ADAMW4_ZIP_SR && m <= ADAMW4_V_PRTN; }
+bool valid_mode(int32_t m) { return m >= ADAMW4_ZIP_SR && m <= ADAMW4_V_ZE_RTN; }
 
 adamw4_status check_hparams(const adamw4_hparams& h) {
     if (h.step < 1 || h.step > int64_t(UINT32_MAX)) return ADAMW4_EINVAL;
@@ -116,7 +116,8 @@ StepArgs step_args(const adamw4_hparams& h) {
     a.t = uint32_t(h.step);
     a.mode = h.mode;
     // codebook of the incoming v: zero-excluding after ZE-EDEN, zero-inclusive after any other
-    a.vin_mode = (((h.prev_mode < 0) ? h.mode : h.prev_mode) == ADAMW4_ZE_EDEN) ? 1 : 0;
+    const int32_t vin = (h.prev_mode < 0) ? h.mode : h.prev_mode;
+    a.vin_mode = (vin == ADAMW4_ZE_EDEN || vin == ADAMW4_V_ZE_RTN) ? 1 : 0;
     a.sr_head = h.sr_head;
     return a;
 }

@@ -52,14 +52,18 @@ typedef enum {
  * The other three are the rules the method is compared with in the pages' controlled study,
  * all on the zero-inclusive codebook ([lav-RO]): V_RTN, nearest level in v (ties low);
  * V_SSR, state-space stochastic rounding (lower level with probability (b-v)/(b-a)); V_PRTN,
- * preconditioner-space round to nearest (the level with the nearest h, ties low).  A v encoded
- * by any mode but ZE-EDEN decodes with the zero-inclusive codebook. */
+ * preconditioner-space round to nearest (the level with the nearest h, ties low).
+ * V_ZE_RTN is the baseline the pages measure against ([lav-ZE]: TorchAO's positive floor;
+ * [lav-ST]: a small positive bottom notch): the zero-excluding codebook, nearest level, the
+ * plain absmax block scale -- ZE-EDEN without its rescale.  A v encoded by ZE-EDEN or V_ZE_RTN
+ * decodes with the zero-excluding codebook, by any other mode with the zero-inclusive one. */
 typedef enum {
     ADAMW4_ZIP_SR = 0,
     ADAMW4_ZE_EDEN = 1,
     ADAMW4_V_RTN = 2,
     ADAMW4_V_SSR = 3,
-    ADAMW4_V_PRTN = 4
+    ADAMW4_V_PRTN = 4,
+    ADAMW4_V_ZE_RTN = 5
 } adamw4_mode;
 
 /* per-tensor flags */
@@ -129,8 +133,8 @@ adamw4_status adamw4_codebook(int32_t which, float out[16]);
 /* Write the initial state of n tensors.  m0[i] / v0[i] are device pointers to numel FP32
  * initial moments of tensor i (16-B aligned); a NULL array or a NULL entry means zeros.
  * Non-zero moments are encoded deterministically (absmax scale, nearest level of NF4 for m and
- * of the codebook of `mode` for v, the zero-inclusive one unless `mode` is ZE-EDEN; ZE-EDEN adds
- * its block rescale); no RNG is used because no
+ * of the codebook of `mode` for v, the zero-excluding one for ZE-EDEN and V_ZE_RTN, else the
+ * zero-inclusive one; ZE-EDEN adds its block rescale); no RNG is used because no
  * step t exists yet.  Only ts[i].numel, flags, state and state_size are used.  m0 and v0 are
  * host arrays of n pointers.  The call waits for its work on `stream` before returning. */
 adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode,

@@ -110,7 +110,7 @@ cases = [
   ("eps subnormal", step([T()], A.hparams(step=1, eps=1e-39)), EINVAL),
   ("lr nan", step([T()], A.hparams(step=1, lr=float("nan"))), EINVAL),
   ("wd inf", step([T()], A.hparams(step=1, weight_decay=float("inf"))), EINVAL),
-  ("mode 5", step([T()], A.hparams(step=1, mode=5)), EINVAL),
+  ("mode 6", step([T()], A.hparams(step=1, mode=6)), EINVAL),
   ("mode -1", step([T()], A.hparams(step=1, mode=-1)), EINVAL),
   ("prev_mode 7", step([T()], A.hparams(step=1, prev_mode=7)), EINVAL),
   ("sr_head 2", step([T()], A.hparams(step=1, sr_head=2)), EINVAL),
@@ -130,7 +130,7 @@ cases = [
   ("second tensor bad", step([T(), T(numel=-1)], good), EINVAL),
   ("init bad mode", L.adamw4_init_state(None, 0, 7, None, None, None), EINVAL),
   ("decode null", L.adamw4_decode_state(None, 0, None, None, None), EINVAL),
-  ("decode bad mode", L.adamw4_decode_state(ctypes.byref(T()), 5, None, None, None), EINVAL),
+  ("decode bad mode", L.adamw4_decode_state(ctypes.byref(T()), 6, None, None, None), EINVAL),
   ("layout null", L.adamw4_state_layout(100, 0, None), EINVAL),
   ("codebook 3", L.adamw4_codebook(3, None), EINVAL),
   ("empty list is a no-op", L.adamw4_step(None, 0, ctypes.byref(good), None), 0),

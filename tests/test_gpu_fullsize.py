@@ -164,3 +164,10 @@ def test_study834m_full(env):
     """834M GPT shapes with FP32 first moments, v by ZIP-SR / state RTN / state SR /
     preconditioner RTN in turn (the controlled study's configuration)."""
     _run(env, "study834m", {1, 2, 3, 4, 5, 40})
+
+
+@pytest.mark.timeout(900)
+def test_baseline130m_full(env):
+    """130M GPT shapes under the baseline v rule (zero-free codebook, round to nearest, absmax
+    scale), from log-uniform initial second moments, across the LM-head SR switch."""
+    _run(env, "baseline130m", {1, 2, 90, 91, 100})

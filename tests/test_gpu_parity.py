@@ -46,10 +46,11 @@ def test_state_layout_and_bytes(env):
         assert all(o % 16 == 0 for o in off if o < 2**63)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
 def test_init_matches_oracle(env, mode):
-    """Deterministic encoding of given initial moments (and of zeros) matches the oracle; every
-    mode but ZE-EDEN encodes v to the nearest level of the zero-inclusive codebook."""
+    """Deterministic encoding of given initial moments (and of zeros) matches the oracle: v to
+    the nearest level of the zero-inclusive codebook, or of the zero-excluding one for ZE-EDEN
+    (plus its rescale) and the baseline."""
     import torch
     from gpu_harness import GpuList, oracle_state, compare_state, say
     A, orc = env
@@ -78,7 +79,7 @@ def test_init_matches_oracle(env, mode):
         compare_state(f"init{i}", n, oracle_state(ss[i], n, flags[i]), ref, None, rep)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 3])
+@pytest.mark.parametrize("mode", [0, 1, 3, 5])
 def test_decode_matches_oracle(env, mode):
     import torch
     from gpu_harness import GpuList, to_np, say
@@ -153,6 +154,22 @@ def test_study_modes(env):
     print({k: v for k, v in rep.items() if "flips" in k and v})
 
 
+def test_baseline_mode(env):
+    """The baseline v rule (zero-excluding codebook, round to nearest, absmax scale) on the
+    ragged mixed list, alone, after and before ZE-EDEN (same codebook) and ZIP-SR (the other
+    one), LM-head SR on and off, zero-gradient blocks, FP32 and BF16 grads."""
+    A = env[0]
+    sizes = [4095, 4096, 4097, 128 * 50 + 3, 7000, 128 * 200, 33333, 300]
+    flags = [0, 0, 0, 0, A.T_NORM, A.T_HEAD, 0, A.T_FP32_M]
+    gdt = ["f32", "bf16", "f32", "bf16", "bf16", "bf16", "f32", "f32"]
+    B, E, Z = A.V_ZE_RTN, A.ZE_EDEN, A.ZIP_SR
+    sched = [(1, B, -1, 0), (2, B, -1, 1), (3, E, B, 1), (4, B, E, 0), (5, Z, B, 0), (6, B, Z, 1),
+             (7, B, -1, 0)]
+    rep = _run_steps(env, sizes, flags, gdt, sched, seed=11)
+    print({k: v for k, v in rep.items() if "flips" in k and v})
+    _run_steps(env, sizes, flags, gdt, [(1, B, -1, 1), (2, B, -1, 0)], seed=12, zero_frac=0.3)
+
+
 def test_fp32_m_tensors(env):
     """Quantized tensors that keep m in FP32 (the controlled study's configuration) next to
     ordinary ones, ragged lengths, head and norm flags, BF16 and FP32 grads, every v mode."""
@@ -162,7 +179,8 @@ def test_fp32_m_tensors(env):
     flags = [F, F, F, F | A.T_NORM, F | A.T_HEAD, 0, F]
     gdt = ["f32", "bf16", "bf16", "f32", "bf16", "f32", "bf16"]
     sched = [(1, A.ZIP_SR, -1, 0), (2, A.V_SSR, A.ZIP_SR, 1), (3, A.V_RTN, A.V_SSR, 0),
-             (4, A.V_PRTN, A.V_RTN, 1), (5, A.ZE_EDEN, A.V_PRTN, 0), (6, A.ZIP_SR, A.ZE_EDEN, 1)]
+             (4, A.V_PRTN, A.V_RTN, 1), (5, A.ZE_EDEN, A.V_PRTN, 0), (6, A.ZIP_SR, A.ZE_EDEN, 1),
+             (7, A.V_ZE_RTN, A.ZIP_SR, 0), (8, A.V_ZE_RTN, -1, 1)]
     rep = _run_steps(env, sizes, flags, gdt, sched, seed=10)
     assert all(v for k, v in rep.items() if k.endswith("m_bitexact"))
 

@@ -82,7 +82,7 @@ class Workload:
     name: str
     specs: tuple
     grad_dtype: str          # "f32" | "bf16"
-    mode_schedule: str       # "zip" | "eden" | "alternate" | "study"
+    mode_schedule: str       # "zip" | "eden" | "alternate" | "study" | "baseline"
     steps: int
     data_seed: int
     grad_kind: str = "normal"   # normal | rowscaled | student_t
@@ -93,13 +93,16 @@ class Workload:
         return sum(s.numel for s in self.specs)
 
     def mode_at(self, t: int) -> int:
-        """v encoder at step t (0 ZIP-SR, 1 ZE-EDEN); 'alternate' = ZIP-SR at odd t."""
+        """v encoder at step t (0 ZIP-SR, 1 ZE-EDEN, 5 the baseline); 'alternate' = ZIP-SR at
+        odd t."""
         if self.mode_schedule == "zip":
             return 0
         if self.mode_schedule == "eden":
             return 1
         if self.mode_schedule == "study":   # ZIP-SR, state RTN, state SR, preconditioner RTN
             return (0, 2, 3, 4)[t % 4]
+        if self.mode_schedule == "baseline":   # zero-free codebook, nearest level, no rescale
+            return 5
         return 0 if t % 2 == 1 else 1
 
     def sr_head_at(self, t: int) -> int:
@@ -119,6 +122,8 @@ WORKLOADS = {
                        grad_kind="student_t"),
     "study834m": Workload("study834m", tuple(with_fp32_m(gpt_list(1536, 24, 50304))), "bf16", "study",
                           40, 1006),
+    "baseline130m": Workload("baseline130m", tuple(gpt_list(768, 12, 50304)), "bf16", "baseline",
+                             100, 1007, v0_kind="loguniform"),
 }
 
 
