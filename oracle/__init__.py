@@ -116,6 +116,7 @@ def lib():
         L.orc_encode_block.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_uint64, ctypes.c_int64,
                                        ctypes.c_uint32, ctypes.c_int64, P, P, P]
+        L.orc_bf16_rne.argtypes = [P, ctypes.c_int64, P]
         _lib = L
     return _lib
 
@@ -136,6 +137,14 @@ def codebook(which: int) -> np.ndarray:
     out = np.zeros(16, np.float32)
     lib().orc_codebook(which, _p(out))
     return out
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns (uint16) of FP32 values, round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, np.uint16)
+    lib().orc_bf16_rne(_p(x), x.size, _p(out))
+    return out.reshape(x.shape)
 
 
 def philox4x32_10(ctr, key) -> np.ndarray:

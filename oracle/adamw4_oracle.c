@@ -649,6 +649,19 @@ void orc_encode_block(const float* x, int nvalid, int rule, float rs2, float eps
     }
 }
 
+/* BF16 copy of FP32 weights (the model-side weights refreshed from the FP32 masters): the
+ * upper half of the binary32 pattern rounded to nearest, ties to even, i.e. adding 0x7FFF plus
+ * the kept half's lowest bit before truncating.  Finite inputs; a value past the largest BF16
+ * rounds to infinity as IEEE rounding does. */
+void orc_bf16_rne(const float* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &x[i], sizeof u);
+        uint32_t keep_lsb = (u >> 16) & 1u;
+        out[i] = (uint16_t)((u + 0x7FFFu + keep_lsb) >> 16);
+    }
+}
+
 /* Threads the block loops use (OpenMP), and a way to set them: bookkeeping for timing runs. */
 int orc_threads(void) { return omp_get_max_threads(); }
 void orc_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }

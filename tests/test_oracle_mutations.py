@@ -48,6 +48,10 @@ MUTANTS = {
     "prtn_threshold": ("codes[j] = (uint8_t)(p >= 0.5f ? k : k + 1);",
                        "codes[j] = (uint8_t)(p >= 0.25f ? k : k + 1);"),
     "fp32m_m_not_updated": ("                m32[i] = e.m;\n", "                m32[i] = m32[i];\n"),
+    "bf16_truncates": ("out[i] = (uint16_t)((u + 0x7FFFu + keep_lsb) >> 16);",
+                       "out[i] = (uint16_t)(u >> 16);"),
+    "bf16_ties_away": ("out[i] = (uint16_t)((u + 0x7FFFu + keep_lsb) >> 16);",
+                       "out[i] = (uint16_t)((u + 0x8000u) >> 16);"),
     "baseline_keeps_zero": ("case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V1, cv, vscale); break;",
                             "case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V0, cv, vscale); break;"),
     "baseline_rescales": ("case ORC_V_ZE_RTN: encode_v_rtn_block(vw, V1, cv, vscale); break;",

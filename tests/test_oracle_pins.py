@@ -717,6 +717,32 @@ def test_tiny_tensors_brute_force(orc):
 
 
 # ---------------------------------------------------------------------------------------------
+# P-16  BF16 copy of the updated weights
+# ---------------------------------------------------------------------------------------------
+
+def test_bf16_copy_matches_torch_rounding(orc):
+    """Round to nearest even into BF16 equals torch's CPU conversion (an independent library
+    routine) on every exponent, exact ties with even and odd kept halves, the values next to
+    ties, subnormals, signed zeros and the overflow edge; plus 2^20 random bit patterns."""
+    import torch
+    rng = np.random.default_rng(61)
+    hi = np.arange(0, 0x7F80, dtype=np.uint32)            # every finite non-negative BF16 word
+    low = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    bits = (hi[:, None] << 16 | low[None, :]).ravel()
+    bits = np.concatenate([bits, bits | 0x80000000,
+                           rng.integers(0, 0x7F800000, 1 << 20, dtype=np.uint32),
+                           np.array([0x7F7FFFFF, 0x7F7F7FFF, 0x7F7F8000, 0xFF7F8000], np.uint32)])
+    x = bits.view(f32)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.bf16_rne(x)
+    assert np.array_equal(got, ref)
+    # spot values: 1 + 2^-8 is a tie with an even kept half (stays 1.0), 1 + 3 * 2^-8 a tie with
+    # an odd one (goes up); the largest float rounds to +inf
+    spot = np.array([1 + 2**-8, 1 + 3 * 2**-8, 3.4028235e38], f32)
+    assert orc.bf16_rne(spot).tolist() == [0x3F80, 0x3F82, 0x7F80]
+
+
+# ---------------------------------------------------------------------------------------------
 # P-11  storage accounting
 # ---------------------------------------------------------------------------------------------
 
