@@ -50,13 +50,25 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(w) -> tuple[int, int, int]:
-    """(bytes per launch, quantized values, FP32-state values)."""
+def shard_len(n: int, shard_of: int) -> int:
+    """Length of rank 0's piece when a tensor of n values is split into shard_of pieces at
+    128-value block boundaries."""
+    if shard_of <= 1:
+        return n
+    return min(n, -(-n // (shard_of * 128)) * 128)
+
+
+def algorithmic_bytes(w, shard_of: int = 1, bf16_copy: bool = False) -> tuple[int, int, int]:
+    """(bytes per launch, quantized values, FP32-state values) of the launch's entries: the
+    whole tensors, or rank 0's pieces with shard_of > 1; a BF16 weight copy adds 2 B/value."""
     gb = 2 if w.grad_dtype == "bf16" else 4
     q = f = total = 0
     for s in w.specs:
-        n, nblk = s.numel, (s.numel + 127) // 128
-        if n >= 4096 and not (s.flags & 1):
+        n = shard_len(s.numel, shard_of)
+        nblk = (n + 127) // 128
+        if bf16_copy:
+            total += 2 * n
+        if s.numel >= 4096 and not (s.flags & 1):
             q += n
             if s.flags & 4:   # FP32 m: w r/w, grad, m r/w, v codes r/w, 2 v-scale words per block
                 total += n * (8 + gb + 8 + 1) + nblk * 8
@@ -76,18 +88,32 @@ def pct(xs, p):
     return s[lo] + (s[hi] - s[lo]) * (k - lo)
 
 
-def setup(w, device):
+def setup(w, device, shard_of: int = 1, bf16_copy: bool = False):
+    """The workload's parameter list with its state; with shard_of > 1, rank 0's piece of every
+    tensor (quantized pieces flagged as shards, keyed by the tensor's index)."""
     import torch
     import workloads as W
     import bit_adamw_step_amd as A
-    params, grads = [], []
+    params, grads, flags = [], [], []
     for i, s in enumerate(w.specs):
-        params.append(W.make_param(s, i, device))
-        grads.append(W.make_grad(w, s, i, 1, device))
-    pl = A.ParamList(params, grads, [s.flags for s in w.specs])
+        L = shard_len(s.numel, shard_of)
+        p = W.make_param(s, i, device)
+        g = W.make_grad(w, s, i, 1, device)
+        params.append(p if L == s.numel else p[:L].clone())
+        grads.append(g if L == s.numel else g[:L].clone())
+        del p, g
+        f = s.flags
+        if shard_of > 1 and A.is_quantized(s.numel, s.flags):
+            f |= A.T_SHARD
+        flags.append(f)
+    copies = [torch.zeros(p.numel(), dtype=torch.bfloat16, device=device) for p in params] \
+        if bf16_copy else None
+    keys = list(range(len(params))) if shard_of > 1 else None
+    pl = A.ParamList(params, grads, flags, bf16_copies=copies, keys=keys)
     v0 = None
     if w.v0_kind != "zeros":
-        v0 = [W.make_v0(w, s, i, device) for i, s in enumerate(w.specs)]
+        v0 = [W.make_v0(w, s, i, device)[:shard_len(s.numel, shard_of)].clone()
+              for i, s in enumerate(w.specs)]
     pl.init(w.mode_at(1), None, v0)
     del v0
     torch.cuda.synchronize()
@@ -101,11 +127,12 @@ def timed_schedule(w, K: int) -> list[int]:
 V_MODES = {"zip": 0, "eden": 1, "rtn": 2, "ssr": 3, "prtn": 4, "baseline": 5}
 
 
-def run_gpu(w, steps: int, warmup: int, device, v_mode: str | None = None):
+def run_gpu(w, steps: int, warmup: int, device, v_mode: str | None = None, shard_of: int = 1,
+            bf16_copy: bool = False):
     import torch
     import bit_adamw_step_amd as A
     mode_at = (lambda t: V_MODES[v_mode]) if v_mode else w.mode_at
-    pl = setup(w, device)
+    pl = setup(w, device, shard_of, bf16_copy)
     stream = torch.cuda.current_stream()
     prev = mode_at(1)
 
@@ -334,6 +361,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 4 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--bf16-copy", action="store_true",
+                    help="the step also writes a BF16 copy of the updated weights")
+    ap.add_argument("--shard-of", type=int, default=1, metavar="N",
+                    help="time rank 0's share of an N-way 128-aligned split of every tensor")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
     if args.summarize_profiles:
@@ -352,7 +383,8 @@ def main():
     device = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
     print(f"# setup {w.name}: {len(w.specs)} tensors, {w.numel} values", file=sys.stderr, flush=True)
-    pl, ts, per, wall = run_gpu(w, args.steps, args.warmup, device, args.v_mode)
+    pl, ts, per, wall = run_gpu(w, args.steps, args.warmup, device, args.v_mode, args.shard_of,
+                                args.bf16_copy)
     print(f"# timed {len(per)} steps: mean {sum(per) / len(per):.4f} ms", file=sys.stderr, flush=True)
     if args.copy_calibration:
         a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=device)
@@ -362,10 +394,11 @@ def main():
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
-    bytes_alg, q, f = algorithmic_bytes(w)
+    bytes_alg, q, f = algorithmic_bytes(w, args.shard_of, args.bf16_copy)
+    values = q + f
     ms = sum(per) / len(per)
     ms_wall = wall * 1000 / len(per)
-    gparams = w.numel * len(per) / wall / 1e9
+    gparams = values * len(per) / wall / 1e9
     achieved = bytes_alg / (ms / 1000) / 1e9
     sr = [p for t, p in zip(ts, per) if w.sr_head_at(t)]
     rtn = [p for t, p in zip(ts, per) if not w.sr_head_at(t)]
@@ -387,7 +420,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "values": w.numel, "tensors": len(w.specs),
+            "workload": w.name, "values": values, "tensors": len(w.specs),
+            "shard_of": args.shard_of, "bf16_copy": args.bf16_copy,
             "quantized_values": q, "fp32_state_values": f, "grad_dtype": w.grad_dtype,
             "v_mode": args.v_mode or w.mode_schedule, "timed_t": [ts[0], ts[-1]],
             "ms_launch_median": round(pct(per, 50), 4), "ms_launch_p10": round(pct(per, 10), 4),
@@ -400,11 +434,12 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profile(w.name)},
+                     "traffic": traffic_from_profile(w.name) if args.shard_of == 1 and
+                     not args.bf16_copy and not args.v_mode else None},
         "ceiling": ceil,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.shard_of == 1:
         out["cpu_baseline"] = cpu_baseline(w, pl, args.cpu_budget)
     print(json.dumps(out), flush=True)
 

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libadamw4.so")
 
 ZIP_SR, ZE_EDEN, V_RTN, V_SSR, V_PRTN, V_ZE_RTN = 0, 1, 2, 3, 4, 5   # adamw4_mode
-T_NORM, T_HEAD, T_FP32_M = 1, 2, 4
+T_NORM, T_HEAD, T_FP32_M, T_SHARD, T_KEYED = 1, 2, 4, 8, 16
 GRAD_F32, GRAD_BF16 = 0, 1
 CB_NF4, CB_V0, CB_V1 = 0, 1, 2
 BLOCK = 128
@@ -33,7 +33,9 @@ class Tensor(ctypes.Structure):
     """adamw4_tensor"""
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("numel", ctypes.c_int64),
                 ("flags", ctypes.c_uint32), ("grad_dtype", ctypes.c_uint32),
-                ("state", ctypes.c_void_p), ("state_size", ctypes.c_size_t)]
+                ("state", ctypes.c_void_p), ("state_size", ctypes.c_size_t),
+                ("param_bf16", ctypes.c_void_p), ("offset", ctypes.c_int64),
+                ("key", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 class HParams(ctypes.Structure):
@@ -101,7 +103,7 @@ def state_layout(numel: int, flags: int = 0) -> tuple[int, int, int, int]:
 
 
 def is_quantized(numel: int, flags: int = 0) -> bool:
-    return numel >= MIN_QUANT and not (flags & T_NORM)
+    return (numel >= MIN_QUANT or bool(flags & T_SHARD)) and not (flags & T_NORM)
 
 
 def codebook(which: int) -> list[float]:
@@ -111,7 +113,8 @@ def codebook(which: int) -> list[float]:
 
 
 def tensor_array(specs) -> ctypes.Array:
-    """ctypes array of adamw4_tensor from (param, grad, numel, flags, grad_dtype, state, size)."""
+    """ctypes array of adamw4_tensor from (param, grad, numel, flags, grad_dtype, state, size
+    [, param_bf16, offset, key]) tuples."""
     arr = (Tensor * len(specs))()
     for i, s in enumerate(specs):
         arr[i] = Tensor(*s)
@@ -158,12 +161,18 @@ class ParamList:
     """Parameters, gradients and optimizer states of one step call (torch device tensors).
 
     params: FP32 CUDA tensors; grads: FP32 or BF16 CUDA tensors of the same numel;
-    flags: per-tensor T_NORM / T_HEAD.  States are allocated here with the library's sizes.
+    flags: per-tensor T_* flags.  States are allocated here with the library's sizes.
+    Optional per-tensor lists (None entries allowed): bf16_copies, BF16 tensors that receive
+    the updated weights; offsets, a shard's start within its whole tensor; keys, RNG keys
+    (sets T_KEYED).
     """
     params: list
     grads: list
     flags: list
     states: list = field(default_factory=list)
+    bf16_copies: list | None = None
+    offsets: list | None = None
+    keys: list | None = None
     _arr: ctypes.Array | None = None
 
     def __post_init__(self):
@@ -178,13 +187,23 @@ class ParamList:
         """Rebuild the tensor array (after grads or states were replaced)."""
         import torch
         specs = []
-        for p, g, f, s in zip(self.params, self.grads, self.flags, self.states):
+        n = len(self.params)
+        copies = self.bf16_copies or [None] * n
+        offsets = self.offsets or [0] * n
+        keys = self.keys or [None] * n
+        for p, g, f, s, c, off, k in zip(self.params, self.grads, self.flags, self.states,
+                                         copies, offsets, keys):
             if p.dtype != torch.float32 or not p.is_contiguous():
                 raise TypeError("params must be contiguous float32")
             if g.numel() != p.numel() or not g.is_contiguous():
                 raise TypeError("grad must be contiguous with the param's numel")
+            if c is not None and (c.dtype != torch.bfloat16 or c.numel() != p.numel()
+                                  or not c.is_contiguous()):
+                raise TypeError("a BF16 copy must be contiguous bfloat16 with the param's numel")
             gd = {torch.float32: GRAD_F32, torch.bfloat16: GRAD_BF16}[g.dtype]
-            specs.append((p.data_ptr(), g.data_ptr(), p.numel(), f, gd, s.data_ptr(), s.numel()))
+            f = f | (T_KEYED if k is not None else 0)
+            specs.append((p.data_ptr(), g.data_ptr(), p.numel(), f, gd, s.data_ptr(), s.numel(),
+                          c.data_ptr() if c is not None else None, off, k or 0, 0))
         self._arr = tensor_array(specs)
 
     @property

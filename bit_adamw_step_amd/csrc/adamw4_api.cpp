@@ -29,7 +29,9 @@ constexpr int kMaxPlans = 8;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
-bool quantized(int64_t n, uint32_t flags) { return n >= kMinQuant && !(flags & ADAMW4_T_NORM); }
+bool quantized(int64_t n, uint32_t flags) {
+    return (n >= kMinQuant || (flags & ADAMW4_T_SHARD)) && !(flags & ADAMW4_T_NORM);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -65,7 +67,13 @@ size_t layout(int64_t n, uint32_t flags, size_t off[4]) {
 adamw4_status check_tensor_common(const adamw4_tensor& t) {
     if (t.numel < 1) return ADAMW4_EINVAL;
     if (t.numel > ADAMW4_MAX_NUMEL) return ADAMW4_ESIZE;
-    if (t.flags & ~uint32_t(ADAMW4_T_NORM | ADAMW4_T_HEAD | ADAMW4_T_FP32_M)) return ADAMW4_EINVAL;
+    if (t.flags & ~uint32_t(ADAMW4_T_NORM | ADAMW4_T_HEAD | ADAMW4_T_FP32_M | ADAMW4_T_SHARD |
+                            ADAMW4_T_KEYED))
+        return ADAMW4_EINVAL;
+    if ((t.flags & ADAMW4_T_SHARD) && (t.flags & ADAMW4_T_NORM)) return ADAMW4_EINVAL;
+    if (t.offset < 0 || (t.offset % kBlock) != 0 || t.offset > ADAMW4_MAX_NUMEL - t.numel)
+        return ADAMW4_EINVAL;
+    if (t.reserved != 0) return ADAMW4_EINVAL;
     if (!t.state) return ADAMW4_EINVAL;
     if (!aligned16(t.state)) return ADAMW4_EALIGN;
     size_t off[4];
@@ -78,7 +86,7 @@ adamw4_status check_tensor_step(const adamw4_tensor& t) {
     if (s != ADAMW4_OK) return s;
     if (!t.param || !t.grad) return ADAMW4_EINVAL;
     if (t.grad_dtype != ADAMW4_GRAD_F32 && t.grad_dtype != ADAMW4_GRAD_BF16) return ADAMW4_EINVAL;
-    if (!aligned16(t.param) || !aligned16(t.grad)) return ADAMW4_EALIGN;
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.param_bf16)) return ADAMW4_EALIGN;
     return ADAMW4_OK;
 }
 
@@ -131,7 +139,8 @@ TensorDesc make_desc(const adamw4_tensor& t, uint32_t pos) {
     d.param = t.param;
     d.grad = t.grad;
     d.numel = t.numel;
-    d.pos = pos;
+    d.pos = (t.flags & ADAMW4_T_KEYED) ? t.key : pos;
+    d.base = t.offset;
     d.flags = 0;
     if (quantized(t.numel, t.flags)) d.flags |= D_QUANT;
     if (t.flags & ADAMW4_T_HEAD) d.flags |= D_HEAD;
@@ -153,6 +162,7 @@ struct Plan {
     uint32_t nchunks = 0;
     uint32_t chunk_units = 0;
     uint32_t ntails = 0;
+    bool extra = false;             // some tensor has a BF16 copy or a shard offset
     size_t tails_off = 0;           // byte offset of the tail list in dbuf
     void* dbuf = nullptr;
     uint64_t last_use = 0;
@@ -239,6 +249,7 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool
     p->nchunks = uint32_t(chunks.size());
     p->chunk_units = cu;
     p->ntails = uint32_t(tails.size());
+    for (const TensorDesc& d : p->descs) p->extra = p->extra || d.wcopy != nullptr || d.base != 0;
     p->tails_off = dbytes + cbytes;
     p->dbuf = dbuf;
     out = p;
@@ -260,6 +271,7 @@ Launch launch_of(const Plan& p, int grid_cap) {
     L.grid = int(std::min<uint64_t>(p.nchunks, uint64_t(std::max(grid_cap, 1))));
     L.tails = reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.dbuf) + p.tails_off);
     L.ntails = p.ntails;
+    L.extra = p.extra;
     return L;
 }
 
@@ -329,7 +341,10 @@ adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hpara
     if (n == 0) return ADAMW4_OK;
 
     std::vector<TensorDesc> descs(static_cast<size_t>(n));
-    for (int32_t i = 0; i < n; ++i) descs[i] = make_desc(ts[i], uint32_t(i));
+    for (int32_t i = 0; i < n; ++i) {
+        descs[i] = make_desc(ts[i], uint32_t(i));
+        descs[i].wcopy = ts[i].param_bf16;
+    }
     const StepArgs a = step_args(*hp);
 
     std::lock_guard<std::mutex> lock(g_mu);

@@ -30,9 +30,11 @@ struct alignas(16) TensorDesc {
     float* s3;
     float* aux0;
     float* aux1;
+    uint16_t* wcopy;   // step: optional BF16 copy of the updated weights
+    int64_t base;      // global index of element 0 (a shard's offset): part of the RNG counter
     int64_t numel;
     uint32_t flags;
-    uint32_t pos;   // position in the caller's list: part of the RNG counter
+    uint32_t pos;      // the tensor's RNG key
 };
 
 // A run of up to `chunk_units` consecutive 128-value units of one tensor.
@@ -67,6 +69,7 @@ struct Launch {
     // hot kernel carries no per-value tail guards.
     const uint32_t* tails;     // device, tensor indices
     uint32_t ntails;
+    bool extra;                // some tensor has a BF16 weight copy or is a shard
 };
 
 hipError_t launch_step(const Launch& L, const StepArgs& a, hipStream_t s);

@@ -70,9 +70,14 @@ typedef enum {
 enum {
     ADAMW4_T_NORM = 1u,  /* normalization-layer tensor: m and v stay FP32 ([lav-ST]) */
     ADAMW4_T_HEAD = 2u,  /* LM-head tensor: its m is rounded stochastically when sr_head is set ([lav-ZE]) */
-    ADAMW4_T_FP32_M = 4u /* a quantized tensor keeps m in FP32 and only v in 4 bits: the pages'
+    ADAMW4_T_FP32_M = 4u,/* a quantized tensor keeps m in FP32 and only v in 4 bits: the pages'
                             controlled study of v rounding rules ([lav-RO]); no effect on tensors
                             that keep both moments in FP32 */
+    ADAMW4_T_SHARD = 8u, /* the entry is a shard of a larger tensor that is quantized (the whole
+                            tensor has >= 4096 elements and is not NORM): the shard is quantized
+                            whatever its own numel.  Not valid with ADAMW4_T_NORM. */
+    ADAMW4_T_KEYED = 16u /* the entry's RNG key is its `key` field rather than its position in
+                            the list */
 };
 
 enum { ADAMW4_GRAD_F32 = 0, ADAMW4_GRAD_BF16 = 1 };
@@ -85,17 +90,36 @@ enum { ADAMW4_CB_NF4 = 0, ADAMW4_CB_V0 = 1, ADAMW4_CB_V1 = 2 };
 #define ADAMW4_MAX_TENSORS 65536
 #define ADAMW4_MAX_NUMEL (((int64_t)1) << 40)
 
-/* One parameter tensor of the step's list.  The tensor's position in the list is part of the
- * RNG key, so keep the list order fixed across steps. */
+/* One parameter tensor, or one shard of a tensor, of the step's list.  The RNG counter of
+ * element i of the entry is (key, offset + i), key being the entry's position in the list or,
+ * with ADAMW4_T_KEYED, its `key` field; so with keys given, stochastic choices depend neither on
+ * the list's order nor on how a tensor is split into shards or calls.
+ *
+ * Shards.  Splitting a tensor into entries [offset, offset + numel) whose offsets are
+ * multiples of 128 and whose lengths are multiples of 128 (the last shard excepted) gives,
+ * with the same key, exactly the bits of the whole-tensor step: every 128-value block and its
+ * scales stay on one entry.  Each shard keeps its own state (adamw4_state_bytes of its own
+ * numel, with ADAMW4_T_SHARD when the whole tensor is quantized). */
 typedef struct {
     float* param;       /* device, [numel] FP32 master weights, updated in place, 16-B aligned */
     const void* grad;   /* device, [numel] FP32 or BF16 gradient (read only), 16-B aligned */
     int64_t numel;      /* 1 .. ADAMW4_MAX_NUMEL */
-    uint32_t flags;     /* ADAMW4_T_NORM | ADAMW4_T_HEAD */
+    uint32_t flags;     /* ADAMW4_T_NORM | ADAMW4_T_HEAD | ADAMW4_T_FP32_M | ADAMW4_T_SHARD |
+                           ADAMW4_T_KEYED */
     uint32_t grad_dtype;/* ADAMW4_GRAD_F32 or ADAMW4_GRAD_BF16 */
     void* state;        /* device, 16-B aligned, persistent optimizer state of this tensor */
     size_t state_size;  /* bytes available at `state`; must be >= adamw4_state_bytes(numel, flags)
                            (ADAMW4_ESIZE otherwise) */
+    uint16_t* param_bf16; /* device, optional (NULL = none), 16-B aligned: [numel] BF16 copy of
+                             the updated weights (round to nearest even), written by adamw4_step
+                             in the same pass, e.g. the model's BF16 weights.  Ignored by init and
+                             decode. */
+    int64_t offset;     /* index of element 0 within the whole tensor (a shard's start): a
+                           multiple of 128, offset + numel <= ADAMW4_MAX_NUMEL; 0 for a whole
+                           tensor */
+    uint32_t key;       /* the tensor's RNG key when ADAMW4_T_KEYED is set (else unused: the key
+                           is the entry's position, so keep the list order fixed across steps) */
+    uint32_t reserved;  /* must be 0 */
 } adamw4_tensor;
 
 typedef struct {
@@ -112,7 +136,7 @@ typedef struct {
 } adamw4_hparams;
 
 /* Size in bytes of one tensor's persistent optimizer state ([lav-ST], [daiwk-LR]).  Pure host
- * function, no device needed.  Quantized tensors (numel >= 4096 and not NORM): m codes and v
+ * function, no device needed.  Quantized tensors (numel >= 4096 and not NORM, or SHARD): m codes and v
  * codes (ceil(numel/2) bytes each, two 4-bit codes per byte, element 2q in the low nibble of
  * byte q), then m scales and v scales (ceil(numel/128) FP32 each); each section starts on a
  * 16-byte boundary.  With ADAMW4_T_FP32_M: FP32 m (numel), v codes, v scales.  Other tensors:

@@ -116,10 +116,21 @@ def compare_weights(name: str, w_gpu: np.ndarray, w_ref: np.ndarray, report: dic
             raise Mismatch(f"{name}: weights differ at {j}: gpu {w_gpu[j]} oracle {w_ref[j]}")
 
 
+def compare_bf16_copy(name: str, copy: np.ndarray, w_ref: np.ndarray, w_gpu: np.ndarray) -> None:
+    """The BF16 copy is the oracle's round-to-nearest-even of the oracle's weights: bit-exact
+    where the weights are (one BF16 step allowed where the weights differ within tolerance)."""
+    exp = orc.bf16_rne(w_ref)
+    same_w = w_gpu.view(np.uint32) == w_ref.view(np.uint32)
+    bad = (copy != exp) & (same_w | (np.abs(copy.astype(np.int32) - exp.astype(np.int32)) > 1))
+    if bad.any():
+        j = np.nonzero(bad)[0][:8]
+        raise Mismatch(f"{name}: BF16 copy differs at {j}: gpu {copy[j]} oracle {exp[j]}")
+
+
 class GpuList:
     """A parameter list on the GPU with its states, plus host snapshots for replay."""
 
-    def __init__(self, sizes, flags, grad_dtypes, device="cuda", seed=0):
+    def __init__(self, sizes, flags, grad_dtypes, device="cuda", seed=0, copies=None):
         import torch
         self.n = list(sizes)
         self.flags = list(flags)
@@ -130,7 +141,11 @@ class GpuList:
             self.params.append((torch.randn(n, generator=g) * 0.02).to(device))
             self.grads.append(torch.zeros(n, dtype=torch.bfloat16 if gd == "bf16" else torch.float32,
                                           device=device))
-        self.pl = A.ParamList(self.params, self.grads, self.flags)
+        # optional BF16 copies of the updated weights (copies[i] True: tensor i gets one)
+        self.copies = [torch.zeros(n, dtype=torch.bfloat16, device=device) if c else None
+                       for n, c in zip(self.n, copies or [False] * len(self.n))]
+        self.pl = A.ParamList(self.params, self.grads, self.flags,
+                              bf16_copies=self.copies if copies else None)
 
     def set_grads(self, t, seed=0, scale=1e-3, zero_frac=0.0):
         import torch
@@ -160,4 +175,6 @@ class GpuList:
             dbg = orc.step_tensor(w, gs[i], st, ohp, pos=i, head=bool(f & A.T_HEAD), dbg=True)
             name = f"{tag}t{i}(n={n},f={f})"
             compare_weights(name, w_now[i], w, report)
+            if self.copies[i] is not None:
+                compare_bf16_copy(name, to_np(self.copies[i]), w, w_now[i])
             compare_state(name, n, oracle_state(s_now[i], n, f), st, dbg, report)

@@ -57,6 +57,18 @@ def test_state_bytes_fp32_m(A):
     assert A.state_bytes(5000, A.T_FP32_M | A.T_NORM) == A.state_bytes(5000, A.T_NORM)
 
 
+def test_state_bytes_shard(A):
+    """A shard of a quantized tensor is quantized whatever its own length (its blocks are the
+    whole tensor's); SHARD has no other effect on the layout."""
+    al = lambda x: (x + 15) // 16 * 16
+    for n in (128, 300, 4095, 4096, 10000):
+        assert A.state_bytes(n, A.T_SHARD) == 2 * al((n + 1) // 2) + 2 * al(4 * ((n + 127) // 128))
+        assert A.is_quantized(n, A.T_SHARD)
+    assert A.state_bytes(5000, A.T_SHARD) == A.state_bytes(5000, 0)
+    assert A.state_bytes(300, A.T_SHARD | A.T_FP32_M) == al(4 * 300) + al(150) + al(12)
+    assert A.state_bytes(300, A.T_SHARD | A.T_KEYED) == A.state_bytes(300, A.T_SHARD)
+
+
 def test_state_bytes_formula(A):
     """Quantized: two code sections of ceil(n/2) bytes and two scale sections of ceil(n/128)
     FP32, 16-byte aligned; FP32 tensors: 2 x 4n bytes."""
@@ -92,9 +104,10 @@ EINVAL, EALIGN, ESIZE, EHIP = -1, -2, -3, -4
 FAKE = 0x7F0000000000          # never dereferenced: every case below fails validation first
 def T(**kw):
     d = dict(param=FAKE, grad=FAKE + 4096, numel=8192, flags=0, grad_dtype=0, state=FAKE + 65536,
-             state_size=A.state_bytes(8192, 0))
+             state_size=A.state_bytes(8192, 0), param_bf16=None, offset=0, key=0, reserved=0)
     d.update(kw)
-    return A.Tensor(d["param"], d["grad"], d["numel"], d["flags"], d["grad_dtype"], d["state"], d["state_size"])
+    return A.Tensor(d["param"], d["grad"], d["numel"], d["flags"], d["grad_dtype"], d["state"],
+                    d["state_size"], d["param_bf16"], d["offset"], d["key"], d["reserved"])
 def step(ts, hp, n=None):
     arr = (A.Tensor * len(ts))(*ts)
     return L.adamw4_step(ctypes.addressof(arr) if ts else None, len(ts) if n is None else n, ctypes.byref(hp), None)
@@ -117,7 +130,13 @@ cases = [
   ("step > 2^32-1", step([T()], A.hparams(step=1 << 32)), EINVAL),
   ("numel 0", step([T(numel=0)], good), EINVAL),
   ("numel too big", step([T(numel=(1 << 40) + 1)], good), ESIZE),
-  ("bad flag", step([T(flags=8)], good), EINVAL),
+  ("bad flag", step([T(flags=32)], good), EINVAL),
+  ("shard of a norm tensor", step([T(flags=A.T_SHARD | A.T_NORM)], good), EINVAL),
+  ("offset not a block multiple", step([T(offset=64)], good), EINVAL),
+  ("negative offset", step([T(offset=-128)], good), EINVAL),
+  ("offset past the limit", step([T(offset=(1 << 40) - 4096)], good), EINVAL),
+  ("reserved set", step([T(reserved=1)], good), EINVAL),
+  ("misaligned bf16 copy", step([T(param_bf16=FAKE + 8192 + 2)], good), EALIGN),
   ("bad dtype", step([T(grad_dtype=2)], good), EINVAL),
   ("null param", step([T(param=0)], good), EINVAL),
   ("null grad", step([T(grad=0)], good), EINVAL),

@@ -1,7 +1,7 @@
 """Out-of-bounds guard: every parameter, gradient and state buffer lives inside a larger device
 allocation whose surrounding bytes hold a random pattern; after steps in both modes (ragged
-lengths, FP32-state tensors, LM-head stochastic rounding, init and decode) the pattern must be
-intact and the results must still match the oracle."""
+lengths, FP32-state tensors, LM-head stochastic rounding, BF16 weight copies, init and decode)
+the pattern must be intact and the results must still match the oracle."""
 import numpy as np
 import pytest
 
@@ -47,14 +47,17 @@ class Guarded:
 
 def test_no_writes_outside_buffers(env):
     import torch
-    from gpu_harness import oracle_state, compare_state, compare_weights, say, to_np
+    from gpu_harness import oracle_state, compare_state, compare_weights, compare_bf16_copy, say, to_np
     A, orc = env
     rng = np.random.default_rng(21)
     sizes = [4095, 4096, 4097, 128 * 50 + 3, 64, 1, 7000, 128 * 40, 33333, 129]
     flags = [0, 0, 0, 0, 0, 0, A.T_NORM, A.T_HEAD, A.T_HEAD, 0]
     gdt = ["f32", "bf16", "bf16", "f32", "bf16", "f32", "bf16", "f32", "bf16", "f32"]
-    guards, params, grads, states, specs = [], [], [], [], []
+    guards, params, grads, states, specs, copies = [], [], [], [], [], []
     for n, f, gd in zip(sizes, flags, gdt):
+        gc = Guarded(2 * n, rng)
+        guards.append(gc)
+        copies.append(gc.view(torch.bfloat16, n))
         gp = Guarded(4 * n, rng)
         gg = Guarded((2 if gd == "bf16" else 4) * n, rng)
         sb = A.state_bytes(n, f)
@@ -66,7 +69,7 @@ def test_no_writes_outside_buffers(env):
         params.append(p)
         grads.append(g)
         states.append(gs.view(torch.uint8, sb))
-    pl = A.ParamList(params, grads, flags, states=states)
+    pl = A.ParamList(params, grads, flags, states=states, bf16_copies=copies)
     m0 = [torch.from_numpy(rng.normal(0, 1e-4, n).astype(np.float32)).cuda() for n in sizes]
     pl.init(A.ZIP_SR, m0, None)
     ostates = [orc.init_state(n, bool(f & A.T_NORM), orc.ZIP_SR, m0[i].cpu().numpy(), None)
@@ -86,6 +89,7 @@ def test_no_writes_outside_buffers(env):
             dbg = orc.step_tensor(ws[i], gh[i], ostates[i], orc.HParams(**kw), pos=i,
                                   head=bool(flags[i] & A.T_HEAD), dbg=True)
             compare_weights(f"t{t}:{i}", to_np(params[i]), ws[i], rep)
+            compare_bf16_copy(f"t{t}:{i}", to_np(copies[i]), ws[i], to_np(params[i]))
             compare_state(f"t{t}:{i}", n, oracle_state(to_np(states[i]), n, flags[i]), ostates[i], dbg, rep)
             ws[i] = to_np(params[i]).copy()          # continue from the GPU's values
             ostates[i] = oracle_state(to_np(states[i]), n, flags[i])
