@@ -196,7 +196,8 @@ def ceiling(q: int, device, reps: int = 5) -> dict | None:
     byts = n * 12 + nb * 16
     del wv, g, mc, vc, sm, sv
     torch.cuda.empty_cache()
-    return {"kernel": "same-byte-mix streaming (12.125 B/value, step access pattern)",
+    return {"kernel": "same-byte-mix streaming (12.125 B/value, step access pattern, "
+                      "non-temporal grad loads)",
             "values": n, "ms": round(ms, 4), "GBs": round(byts / (ms / 1000) / 1e9, 1),
             "grid": grid, "chunk_blocks": chunk}
 
