@@ -43,6 +43,32 @@ def test_exports_every_declared_function(A):
         assert re.search(r"\bT " + n + r"\b", out), n
 
 
+def test_struct_layouts_match_header(A, tmp_path):
+    """The binding's ctypes structures have the header's sizes and field offsets (checked with
+    a host C program compiled against include/adamw4.h)."""
+    import ctypes
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = {"adamw4_tensor": [f for f, _ in A.Tensor._fields_],
+              "adamw4_hparams": [f for f, _ in A.HParams._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "adamw4.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(root, "include"), "-o", str(exe), str(src)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for st, cls in (("adamw4_tensor", A.Tensor), ("adamw4_hparams", A.HParams)):
+        assert int(got[st]) == ctypes.sizeof(cls), st
+        for f in fields[st]:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
 def test_state_bytes_fp32_m(A):
     """FP32-m tensors: FP32 m, then v codes, then v scales, 16-byte aligned; no m scales."""
     for n in (4096, 4097, 12345, 1 << 20):
