@@ -199,3 +199,37 @@ def test_keys_make_list_order_irrelevant(env):
             sb = oracle_state(to_np(fwd.states[i]), sizes[i], flags[i])
             for name in ("mcodes", "vcodes", "mscale", "vscale"):
                 assert np.array_equal(getattr(sa, name), getattr(sb, name)), (t, i, name)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
+def test_extra_kernel_equals_plain(env, mode):
+    """Lists with BF16 copies run the step kernel's second instantiation: for every v rule it
+    gives the plain kernel's weights and state bit for bit, and the copies are the weights'
+    rounding (oracle's bf16_rne)."""
+    import torch
+    from gpu_harness import GpuList, oracle_state, to_np, say
+    A, orc = env
+    sizes = [4096 * 5 + 128 * 3, 128 * 77 + 5, 6000, 9000, 300]
+    flags = [0, 0, A.T_NORM, A.T_HEAD, 0]
+    gdt = ["bf16", "f32", "bf16", "bf16", "f32"]
+    plain = GpuList(sizes, flags, gdt, seed=51)
+    extra = GpuList(sizes, flags, gdt, seed=51, copies=[True] * len(sizes))
+    plain.pl.init(mode)
+    extra.pl.init(mode)
+    for t in (1, 2, 3):
+        plain.set_grads(t, seed=51)
+        extra.set_grads(t, seed=51)
+        hp = A.hparams(step=t, mode=mode, sr_head=int(t == 3), seed=8)
+        say(f"extra vs plain: mode={mode} t={t}")
+        plain.pl.step(hp)
+        extra.pl.step(hp)
+        torch.cuda.synchronize()
+        for i, n in enumerate(sizes):
+            wp, we = to_np(plain.params[i]), to_np(extra.params[i])
+            assert np.array_equal(wp.view(np.uint32), we.view(np.uint32)), (mode, t, i)
+            assert np.array_equal(to_np(extra.copies[i]), orc.bf16_rne(we)), (mode, t, i)
+            sp = oracle_state(to_np(plain.pl.states[i]), n, flags[i])
+            se = oracle_state(to_np(extra.pl.states[i]), n, flags[i])
+            for k in ("mcodes", "vcodes", "mscale", "vscale", "m", "v"):
+                a, b = getattr(sp, k), getattr(se, k)
+                assert (a is None and b is None) or np.array_equal(a, b), (mode, t, i, k)
