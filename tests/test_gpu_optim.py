@@ -119,10 +119,12 @@ def _run(A, orc, optim, dtype, schedule, seed, total_steps=None):
 
 
 def test_optimizer_steps_match_oracle_fp32(env):
+    """FP32 parameters through every v rule (mode switches included) and the LM-head switch."""
+    import torch
     A, orc, optim = env
     sched = ["zip-sr", "zip-sr", "ze-eden", "ze-eden", "state-sr", "zip-sr", "baseline",
              "precond-rtn", "zip-sr", "zip-sr"]
-    _, _, rep = _run(A, orc, optim, __import__("torch").float32, sched, seed=3, total_steps=10)
+    _, _, rep = _run(A, orc, optim, torch.float32, sched, seed=3, total_steps=10)
     assert all(v for k, v in rep.items() if isinstance(k, str) and k.endswith("w_bitexact"))
 
 
