@@ -1,6 +1,7 @@
 """Benchmark of the fused 4-bit AdamW step (ZIP-SR / ZE-EDEN) on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2b7]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2b7] [--v-mode RULE]
+                [--bf16-copy] [--shard-of N] [--no-cpu-baseline] [--no-ceiling]
 
 One step = one adamw4_step call over the whole parameter list (every value: decode, AdamW,
 weight update, requantize, pack), inputs resident in HBM.  The default workload is the
@@ -19,6 +20,8 @@ same access pattern with trivial arithmetic; its rate is the practical HBM ceili
 byte mix on the GPU at hand.
 cpu_baseline: the CPU oracle (test infrastructure, timed here only) stepping the same list,
 tensor by tensor from host copies of the GPU's current state, until a time budget is spent.
+--v-mode runs every step with one v rule; --bf16-copy adds the fused BF16 weight copy (2 B per
+value more); --shard-of N times rank 0's share of an N-way 128-aligned split of every tensor.
 
 python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR [--workload W]
 reads rocprofv3 CSV output (kernel trace + stats, FETCH_SIZE pass, WRITE_SIZE pass, each from
