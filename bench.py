@@ -375,8 +375,9 @@ def main():
         summarize_profiles(*args.summarize_profiles, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the 4-bit AdamW step needs no communication and every "
-              "box here has a single MI355X; run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the 4-bit AdamW step needs no communication, a sharded "
+              "run is N copies of rank 0's share (see --shard-of); run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
