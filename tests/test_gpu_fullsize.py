@@ -171,3 +171,50 @@ def test_baseline130m_full(env):
     """130M GPT shapes under the baseline v rule (zero-free codebook, round to nearest, absmax
     scale), from log-uniform initial second moments, across the LM-head SR switch."""
     _run(env, "baseline130m", {1, 2, 90, 91, 100})
+
+
+@pytest.mark.timeout(900)
+def test_llama2b7_rank0_share_equals_whole(env):
+    """Rank 0's share of an 8-way split of the 2.7B list (the shape `bench.py --shard-of 8`
+    times: the first 128-aligned eighth of every tensor, quantized pieces flagged as shards,
+    keyed by tensor index) stepped in one call, against the whole list stepped in another: the
+    share's weights, codes and scales equal the whole tensors' leading slices bit for bit over
+    ZIP-SR steps with and without LM-head stochastic rounding (compared on the device)."""
+    import torch
+    import bench
+    import workloads as W
+    from gpu_harness import say
+    A, orc = env
+    w = W.WORKLOADS["llama2b7"]
+    say(f"rank-0 share vs whole: {len(w.specs)} tensors, {w.numel} values")
+    whole, _ = _setup(w, A)
+    lens = [bench.shard_len(s.numel, 8) for s in w.specs]
+    flags = [s.flags | (A.T_SHARD if A.is_quantized(s.numel, s.flags) else 0) for s in w.specs]
+    share = A.ParamList([whole.params[i][:L].clone() for i, L in enumerate(lens)],
+                        [whole.grads[i][:L].clone() for i, L in enumerate(lens)], flags,
+                        keys=list(range(len(lens))))
+    share.init(A.ZIP_SR)
+    dev = torch.device("cuda:0")
+    for t in (1, 2, 3):
+        if t > 1:
+            for i, s in enumerate(w.specs):
+                W.make_grad(w, s, i, t, dev, out=whole.grads[i])
+                share.grads[i].copy_(whole.grads[i][:lens[i]])
+        hp = A.hparams(step=t, mode=A.ZIP_SR, sr_head=int(t == 3), seed=0)
+        say(f"  step t={t} sr_head={int(t == 3)}")
+        whole.step(hp)
+        share.step(hp)
+        torch.cuda.synchronize()
+        for i, (s, L) in enumerate(zip(w.specs, lens)):
+            assert torch.equal(share.params[i].view(torch.int32),
+                               whole.params[i][:L].view(torch.int32)), (t, i, "weights")
+            ow, osh = A.state_layout(s.numel, s.flags), A.state_layout(L, flags[i])
+            if A.is_quantized(s.numel, s.flags):
+                nb = (L + 127) // 128
+                secs = [(0, (L + 1) // 2), (1, (L + 1) // 2), (2, 4 * nb), (3, 4 * nb)]
+            else:
+                secs = [(0, 4 * L), (1, 4 * L)]
+            for k, length in secs:
+                a = share.states[i][osh[k]:osh[k] + length]
+                b = whole.states[i][ow[k]:ow[k] + length]
+                assert torch.equal(a, b), (t, i, "state section", k)
