@@ -98,3 +98,59 @@ def test_no_writes_outside_buffers(env):
         gm, gv = Guarded(4 * n, rng), Guarded(4 * n, rng)
         A.decode_state(pl.array[i], 0, gm.view(torch.float32, n).data_ptr(), gv.view(torch.float32, n).data_ptr())
         assert gm.intact() and gv.intact()
+
+
+def test_shards_stay_inside_their_buffers(env):
+    """Shard entries (offsets into their whole tensors, RNG keys, short shards kept quantized,
+    an FP32-m shard, ragged last blocks) between canaries: after four steps the canaries are
+    intact and every step matches the oracle's step of the same element range."""
+    import torch
+    from gpu_harness import oracle_state, compare_state, compare_weights, compare_bf16_copy, say, to_np
+    A, orc = env
+    rng = np.random.default_rng(22)
+    f32 = np.float32
+    ents = [(300, A.T_SHARD, 1280), (128 * 5 + 7, A.T_SHARD | A.T_HEAD, 128 * 33),
+            (4095, A.T_SHARD, 0), (1000, A.T_SHARD | A.T_FP32_M, 256), (129, A.T_SHARD, 128 * 7)]
+    keys = [11, 12, 13, 14, 15]
+    guards, params, grads, states, copies = [], [], [], [], []
+    for n, f, off in ents:
+        gp, gg, gc = Guarded(4 * n, rng), Guarded(2 * n, rng), Guarded(2 * n, rng)
+        sb = A.state_bytes(n, f)
+        gs = Guarded(sb, rng)
+        p = gp.view(torch.float32, n)
+        p.copy_(torch.from_numpy(rng.normal(0, 0.02, n).astype(f32)))
+        guards += [gp, gg, gs, gc]
+        params.append(p)
+        grads.append(gg.view(torch.bfloat16, n))
+        states.append(gs.view(torch.uint8, sb))
+        copies.append(gc.view(torch.bfloat16, n))
+    pl = A.ParamList(params, grads, [f for _, f, _ in ents], states=states, bf16_copies=copies,
+                     offsets=[o for _, _, o in ents], keys=keys)
+    pl.init(A.ZIP_SR)
+    assert all(gd.intact() for gd in guards), "canary overwritten by init"
+    ws = [to_np(p).copy() for p in params]
+    ostates = []
+    for n, f, _ in ents:
+        nb = (n + 127) // 128
+        z8, zs = np.zeros((n + 1) // 2, np.uint8), np.zeros(nb, f32)
+        if f & A.T_FP32_M:
+            ostates.append(orc.State(True, None, z8.copy(), None, zs.copy(), m=np.zeros(n, f32)))
+        else:
+            ostates.append(orc.State(True, z8.copy(), z8.copy(), zs.copy(), zs.copy()))
+    for t, mode, prev, srh in [(1, 0, -1, 1), (2, 3, 0, 1), (3, 1, 3, 0), (4, 0, 1, 1)]:
+        for g in grads:
+            g.copy_(torch.from_numpy(rng.normal(0, 1e-3, g.numel()).astype(f32)).to(g.dtype))
+        kw = dict(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=4)
+        gh = [to_np(g).copy() for g in grads]
+        say(f"guarded shard step t={t} mode={mode}")
+        pl.step(A.hparams(**kw))
+        assert all(gd.intact() for gd in guards), f"canary overwritten at step {t}"
+        rep = {}
+        for i, (n, f, off) in enumerate(ents):
+            dbg = orc.step_tensor(ws[i], gh[i], ostates[i], orc.HParams(**kw), pos=keys[i],
+                                  head=bool(f & A.T_HEAD), e0=off, n=off + n, dbg=True)
+            compare_weights(f"t{t}:{i}", to_np(params[i]), ws[i], rep)
+            compare_bf16_copy(f"t{t}:{i}", to_np(copies[i]), ws[i], to_np(params[i]))
+            compare_state(f"t{t}:{i}", n, oracle_state(to_np(states[i]), n, f), ostates[i], dbg, rep)
+            ws[i] = to_np(params[i]).copy()
+            ostates[i] = oracle_state(to_np(states[i]), n, f)
