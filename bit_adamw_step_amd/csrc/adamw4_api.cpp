@@ -215,7 +215,11 @@ uint64_t plan_units(const TensorDesc& d, bool split_tails) {
 adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool split_tails,
                          Plan*& out) {
     uint64_t total_units = 0;
-    for (const TensorDesc& d : descs) total_units += plan_units(d, split_tails);
+    for (const TensorDesc& d : descs) {
+        // chunk starts are 32-bit block indices (2^32 blocks = 2^39 values per tensor)
+        if (plan_units(d, split_tails) > uint64_t(UINT32_MAX)) return ADAMW4_ESIZE;
+        total_units += plan_units(d, split_tails);
+    }
     const uint32_t cu = pick_chunk_units(total_units, cus);
     std::vector<Chunk> chunks;
     std::vector<uint32_t> tails;

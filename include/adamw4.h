@@ -88,7 +88,7 @@ enum { ADAMW4_CB_NF4 = 0, ADAMW4_CB_V0 = 1, ADAMW4_CB_V1 = 2 };
 #define ADAMW4_BLOCK 128        /* values per FP32 block scale ([lav-ST]) */
 #define ADAMW4_MIN_QUANT 4096   /* tensors with fewer elements keep FP32 m, v ([daiwk-LR]) */
 #define ADAMW4_MAX_TENSORS 65536
-#define ADAMW4_MAX_NUMEL (((int64_t)1) << 40)
+#define ADAMW4_MAX_NUMEL (((int64_t)1) << 38)   /* 2^38 values (1 TiB of FP32 weights) */
 
 /* One parameter tensor, or one shard of a tensor, of the step's list.  The RNG counter of
  * element i of the entry is (key, offset + i), key being the entry's position in the list or,
