@@ -170,8 +170,9 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
  * -- weights use the unquantized m', v' -- then per 128-value block: absmax scales, m to NF4
  * (round to nearest, or state-space stochastic rounding on HEAD tensors when sr_head), v by
  * the encoder of hp->mode, nibble packing.  FP32 tensors run the same AdamW on FP32 m, v.  Stochastic
- * choices draw u in [0,1) from Philox4x32-10 keyed by seed with counter
- * (i>>2, stream<<31 | (i>>2)>>32, tensor position, t); the lower level is kept iff u < p.
+ * choices draw u = (word >> 8) 2^-24 in [0,1) from Philox4x32-10 keyed by seed with counter
+ * (j mod 2^32, stream<<31 | j>>32, tensor key, t), j = (offset + i) >> 2, word i & 3, stream 0
+ * for v and 1 for the LM head's m; the lower level is kept iff u < p.
  * ts: host array of n tensors (n = 0 is a no-op).  The whole list is one kernel launch, plus
  * one small launch for the partial last blocks when a quantized tensor's numel is not a
  * multiple of 128. */
