@@ -231,3 +231,45 @@ def test_run_twice_bit_identical(env):
         outs.append([x.clone() for x in gl.params + gl.pl.states])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_random_lists(env):
+    """Twelve seeded random lists (lengths from 1 to 3e5 around the 128-block and 4096-value
+    boundaries, random NORM / HEAD / FP32_M flags and grad dtypes) stepped under random v-rule
+    schedules with the LM-head switch on and off: every step replayed on the oracle."""
+    A = env[0]
+    rng = np.random.default_rng(2024)
+    for case in range(12):
+        k = int(rng.integers(1, 9))
+        sizes = []
+        for _ in range(k):
+            kind = rng.integers(0, 4)
+            if kind == 0:
+                sizes.append(int(rng.integers(1, 4096)))
+            elif kind == 1:
+                sizes.append(4096 + int(rng.integers(-2, 3)) * int(rng.integers(0, 200)))
+            elif kind == 2:
+                sizes.append(128 * int(rng.integers(32, 400)) + int(rng.integers(0, 128)))
+            else:
+                sizes.append(int(rng.integers(4096, 300000)))
+        sizes = [max(1, n) for n in sizes]
+        flags = []
+        for _ in sizes:
+            f = 0
+            r = rng.random()
+            if r < 0.15:
+                f |= A.T_NORM
+            elif r < 0.3:
+                f |= A.T_FP32_M
+            if rng.random() < 0.2:
+                f |= A.T_HEAD
+            flags.append(f)
+        gdt = [("bf16" if rng.random() < 0.6 else "f32") for _ in sizes]
+        modes = [int(m) for m in rng.integers(0, 6, 3)]
+        sched = []
+        prev = -1
+        for t, m in enumerate(modes, start=1):
+            sched.append((t, m, prev if t > 1 else -1, int(rng.random() < 0.5)))
+            prev = m
+        _run_steps(env, sizes, flags, gdt, sched, seed=100 + case,
+                   zero_frac=0.2 if case % 3 == 0 else 0.0)
