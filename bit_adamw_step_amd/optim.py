@@ -1,8 +1,8 @@
 """``torch.optim.Optimizer`` front end of the fused 4-bit AdamW step.
 
-The step itself is one library call per parameter group (``adamw4_step``); this module only
-keeps the per-parameter state buffers, builds the tensor lists and carries the step counter,
-the v encoder and the LM-head switch between calls.
+The step itself is one library call (``adamw4_step``) per set of groups sharing their
+hyperparameters; this module only keeps the per-parameter state buffers, builds the tensor
+lists and carries the step counter, the v encoder and the LM-head switch between calls.
 
 Methods (daiwk.github.io "ZIP-SR / ZE-EDEN: 4-bit AdamW state quantization", "Core equation"
 and "Paper method and evidence"; learnaivisually.com "ZIP-SR 4-bit AdamW", ZE-EDEN / LM-head
@@ -101,13 +101,17 @@ class AdamW4bit(torch.optim.Optimizer):
 
     @torch.no_grad()
     def step(self, closure=None):
+        """One optimizer step.  Groups that share their hyperparameters, step count and v
+        encoder (e.g. weights, norms and the LM head of one model) go to the library in one
+        call, i.e. one kernel launch; each tensor keeps its own flags and RNG key."""
         loss = None
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
         keys = self._keys()
         stream = torch.cuda.current_stream()
-        for gi, group in enumerate(self.param_groups):
+        batches: dict[tuple, list] = {}
+        for group in self.param_groups:
             mode = mode_id(group["mode"])
             flags = self._flags(group)
             ps = [p for p in group["params"] if p.grad is not None]
@@ -117,8 +121,7 @@ class AdamW4bit(torch.optim.Optimizer):
             for p in fresh:
                 self._init_param_state(p, flags, mode)
             if fresh:
-                arr = self._array(fresh, flags, keys)
-                A.init_state(arr, mode, stream=stream)
+                A.init_state(self._array([(p, flags) for p in fresh], keys), mode, stream=stream)
             t = self.state[ps[0]]["step"] + 1
             prev = self.state[ps[0]]["v_mode"]
             for p in ps:
@@ -127,21 +130,24 @@ class AdamW4bit(torch.optim.Optimizer):
                     raise RuntimeError("parameters of one group must share their step count and "
                                        "v encoder (add new parameters as a new group)")
             b1, b2 = group["betas"]
-            hp = A.hparams(step=t, lr=group["lr"], beta1=b1, beta2=b2, eps=group["eps"],
-                           weight_decay=group["weight_decay"], mode=mode, prev_mode=prev,
-                           sr_head=sr_head_at(t, self.total_steps), seed=self.seed)
-            A.step(self._array(ps, flags, keys), hp, stream)
-            for p in ps:
+            hkey = (t, float(group["lr"]), float(b1), float(b2), float(group["eps"]),
+                    float(group["weight_decay"]), mode, prev)
+            batches.setdefault(hkey, []).extend((p, flags) for p in ps)
+        for (t, lr, b1, b2, eps, wd, mode, prev), items in batches.items():
+            hp = A.hparams(step=t, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, mode=mode,
+                           prev_mode=prev, sr_head=sr_head_at(t, self.total_steps), seed=self.seed)
+            A.step(self._array(items, keys), hp, stream)
+            for p, _ in items:
                 st = self.state[p]
                 st["step"] = t
                 st["v_mode"] = mode
         return loss
 
-    def _array(self, ps, flags: int, keys: dict):
-        """adamw4_tensor array for params ps (the tensors it points into are held by the
-        parameters, their gradients and the optimizer state)."""
+    def _array(self, items, keys: dict):
+        """adamw4_tensor array for (param, flags) pairs (the tensors it points into are held by
+        the parameters, their gradients and the optimizer state)."""
         specs = []
-        for p in ps:
+        for p, flags in items:
             g = p.grad
             if g.numel() != p.numel() or not g.is_contiguous():
                 raise ValueError("gradients must be contiguous with the parameter's numel")
