@@ -61,6 +61,7 @@ class AdamW4bit(torch.optim.Optimizer):
                 self._check_param(p)
         self.seed = int(seed)
         self.total_steps = total_steps
+        self._arrays: dict = {}   # pointer signature -> tensor array of the last few calls
 
     @staticmethod
     def _check_param(p: torch.Tensor) -> None:
@@ -136,12 +137,31 @@ class AdamW4bit(torch.optim.Optimizer):
         for (t, lr, b1, b2, eps, wd, mode, prev), items in batches.items():
             hp = A.hparams(step=t, lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, mode=mode,
                            prev_mode=prev, sr_head=sr_head_at(t, self.total_steps), seed=self.seed)
-            A.step(self._array(items, keys), hp, stream)
+            A.step(self._cached_array(items, keys), hp, stream)
             for p, _ in items:
                 st = self.state[p]
                 st["step"] = t
                 st["v_mode"] = mode
         return loss
+
+    def _cached_array(self, items, keys: dict):
+        """The tensor array of a batch, rebuilt only when a pointer, flag or key changed (grads
+        are usually reallocated at the same addresses every step)."""
+        sig = []
+        for p, flags in items:
+            st = self.state[p]
+            m = st.get("master")
+            sig.append((p.data_ptr(), p.grad.data_ptr(), p.grad.dtype, p.numel(),
+                        st["packed"].data_ptr(), 0 if m is None else m.data_ptr(), flags,
+                        keys[id(p)]))
+        sig = tuple(sig)
+        arr = self._arrays.get(sig)
+        if arr is None:
+            arr = self._array(items, keys)
+            if len(self._arrays) >= 8:
+                self._arrays.pop(next(iter(self._arrays)))
+            self._arrays[sig] = arr
+        return arr
 
     def _array(self, items, keys: dict):
         """adamw4_tensor array for (param, flags) pairs (the tensors it points into are held by
@@ -209,3 +229,4 @@ class AdamW4bit(torch.optim.Optimizer):
         if extra:
             self.seed = int(extra["seed"])
             self.total_steps = extra["total_steps"]
+        self._arrays.clear()
