@@ -1,7 +1,7 @@
 """Benchmark of the fused 4-bit AdamW step (ZIP-SR / ZE-EDEN) on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2b7] [--v-mode RULE]
-                [--bf16-copy] [--shard-of N] [--no-cpu-baseline] [--no-ceiling]
+                [--bf16-copy] [--shard-of N] [--optimizer] [--no-cpu-baseline] [--no-ceiling]
 
 One step = one adamw4_step call over the whole parameter list (every value: decode, AdamW,
 weight update, requantize, pack), inputs resident in HBM.  The default workload is the
@@ -21,7 +21,9 @@ byte mix on the GPU at hand.
 cpu_baseline: the CPU oracle (test infrastructure, timed here only) stepping the same list,
 tensor by tensor from host copies of the GPU's current state, until a time budget is spent.
 --v-mode runs every step with one v rule; --bf16-copy adds the fused BF16 weight copy (2 B per
-value more); --shard-of N times rank 0's share of an N-way 128-aligned split of every tensor.
+value more); --shard-of N times rank 0's share of an N-way 128-aligned split of every tensor;
+--optimizer adds an "optimizer" object: the torch front end's opt.step() on the list as a BF16
+model (GPU and host time).
 
 python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR [--workload W]
 reads rocprofv3 CSV output (kernel trace + stats, FETCH_SIZE pass, WRITE_SIZE pass, each from
@@ -162,6 +164,48 @@ def run_gpu(w, steps: int, warmup: int, device, v_mode: str | None = None, shard
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in ev]   # ms per launch
     return pl, ts, per, wall
+
+
+def run_optimizer(w, steps: int, warmup: int, device) -> dict:
+    """The torch front end end to end on the workload as a BF16 model: BF16 parameters and
+    grads, FP32 masters in the optimizer state, norm and LM-head tensors in their own groups
+    (one library call for all three).  Times opt.step() on the GPU (events) and on the host."""
+    import torch
+    import workloads as W
+    from bit_adamw_step_amd.optim import AdamW4bit
+    params, groups = [], {"plain": [], "norm": [], "head": []}
+    for i, s in enumerate(w.specs):
+        p = W.make_param(s, i, device).to(torch.bfloat16)
+        p.grad = W.make_grad(w, s, i, 1, device).to(torch.bfloat16)
+        params.append(p)
+        groups["norm" if s.flags & 1 else "head" if s.flags & 2 else "plain"].append(p)
+    opt = AdamW4bit([{"params": groups["plain"]}, {"params": groups["norm"], "norm": True},
+                     {"params": groups["head"], "head": True}], lr=1e-3, weight_decay=0.1,
+                    mode="zip-sr", total_steps=w.steps, seed=0)
+    for _ in range(warmup):
+        opt.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    host = []
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        h0 = time.perf_counter()
+        opt.step()
+        host.append(time.perf_counter() - h0)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu = [a.elapsed_time(b) for a, b in ev]
+    n = sum(p.numel() for p in params)
+    return {"values": n, "gpu_ms_median": round(pct(gpu, 50), 4),
+            "host_ms_median": round(1000 * pct(host, 50), 4),
+            "wall_ms_per_step": round(1000 * wall / steps, 4),
+            "bytes_per_value": 14.125,
+            "note": "BF16 params and grads, FP32 masters; 14.125 B/value (master r/w 8, BF16 copy 2, "
+                    "grad 2, codes 2, scales 0.125)"}
 
 
 def ceiling(q: int, device, reps: int = 5) -> dict | None:
@@ -369,6 +413,8 @@ def main():
                     help="the step also writes a BF16 copy of the updated weights")
     ap.add_argument("--shard-of", type=int, default=1, metavar="N",
                     help="time rank 0's share of an N-way 128-aligned split of every tensor")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="also time the torch front end end to end on the workload as a BF16 model")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
     args = ap.parse_args()
     if args.summarize_profiles:
@@ -446,6 +492,10 @@ def main():
     }
     if not args.no_cpu_baseline and args.shard_of == 1:
         out["cpu_baseline"] = cpu_baseline(w, pl, args.cpu_budget)
+    if args.optimizer:
+        del pl
+        torch.cuda.empty_cache()
+        out["optimizer"] = run_optimizer(w, args.steps, args.warmup, device)
     print(json.dumps(out), flush=True)
 
 
