@@ -53,8 +53,8 @@ struct StepArgs {
     float beta1, beta2, eps;
     uint32_t seed_lo, seed_hi;
     uint32_t t;
-    int32_t mode;      // v encoder: 0 ZIP-SR, 1 ZE-EDEN
-    int32_t vin_mode;  // codebook of the incoming v
+    int32_t mode;      // v encoder (adamw4_mode)
+    int32_t vin_mode;  // codebook of the incoming v: 0 V0, 1 V1
     int32_t sr_head;   // HEAD tensors' m stochastically rounded this step
 };
 
