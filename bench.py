@@ -16,8 +16,9 @@ launch stream.  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SI
 scaled by the counters' reading on a copy of known size, stored in
 profiles/counters_<workload>.json and used only while the kernel source is unchanged.
 ceiling: a streaming kernel (libadamw4_ceiling.so) that moves the same bytes per value in the
-same access pattern with trivial arithmetic; its rate is the practical HBM ceiling for this
-byte mix on the GPU at hand.
+same access pattern with trivial arithmetic, at its best of two grid sizes: what a plain
+streaming kernel reaches with this byte mix on the GPU at hand (the step can come close to it
+or pass it; it is a reference point, not a bound).
 cpu_baseline: the CPU oracle (test infrastructure, timed here only) stepping the same list,
 tensor by tensor from host copies of the GPU's current state, until a time budget is spent.
 --v-mode runs every step with one v rule; --bf16-copy adds the fused BF16 weight copy (2 B per
@@ -209,7 +210,8 @@ def run_optimizer(w, steps: int, warmup: int, device) -> dict:
 
 
 def ceiling(q: int, device, reps: int = 5) -> dict | None:
-    """Time the same-byte-mix streaming kernel over q quantized values in flat buffers."""
+    """Time the same-byte-mix streaming kernel over q quantized values in flat buffers, at 2
+    and 4 workgroups per CU (256-block chunks); report the faster."""
     import torch
     if not os.path.exists(CEILING_LIB) or q < 128:
         return None
@@ -227,24 +229,30 @@ def ceiling(q: int, device, reps: int = 5) -> dict | None:
     sm = torch.ones(nb, dtype=torch.float32, device=device)
     sv = torch.ones(nb, dtype=torch.float32, device=device)
     stream = torch.cuda.current_stream()
-    grid, chunk = 1024, 256
-    args = [wv.data_ptr(), g.data_ptr(), mc.data_ptr(), vc.data_ptr(), sm.data_ptr(), sv.data_ptr(),
-            nb, grid, chunk, ctypes.c_void_p(stream.cuda_stream)]
-    for _ in range(2):
-        if L.adamw4_ceiling_mix(*args) != 0:
-            raise RuntimeError("ceiling kernel launch failed")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
-        L.adamw4_ceiling_mix(*args)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    best = None
+    for grid, chunk in ((2 * cus, 256), (4 * cus, 256)):
+        args = [wv.data_ptr(), g.data_ptr(), mc.data_ptr(), vc.data_ptr(), sm.data_ptr(),
+                sv.data_ptr(), nb, grid, chunk, ctypes.c_void_p(stream.cuda_stream)]
+        for _ in range(2):
+            if L.adamw4_ceiling_mix(*args) != 0:
+                raise RuntimeError("ceiling kernel launch failed")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            L.adamw4_ceiling_mix(*args)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+        if best is None or ms < best[0]:
+            best = (ms, grid, chunk)
+    ms, grid, chunk = best
     byts = n * 12 + nb * 16
     del wv, g, mc, vc, sm, sv
     torch.cuda.empty_cache()
     return {"kernel": "same-byte-mix streaming (12.125 B/value, step access pattern, "
-                      "non-temporal grad loads)",
+                      "non-temporal weights and grads)",
             "values": n, "ms": round(ms, 4), "GBs": round(byts / (ms / 1000) / 1e9, 1),
             "grid": grid, "chunk_blocks": chunk}
 

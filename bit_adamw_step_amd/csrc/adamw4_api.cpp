@@ -195,11 +195,12 @@ adamw4_status device_info(int dev, DeviceInfo& out) {
     return ADAMW4_OK;
 }
 
-// Chunk size: 64 units (8192 values) for large lists; smaller when the list is too small to
-// give every CU several chunks, but never below one workgroup iteration (16 units).
+// Chunk size: 256 units (32768 values) for large lists, so each workgroup streams long runs
+// of consecutive lines; smaller when the list is too small to give every CU several chunks,
+// but never below one workgroup iteration (16 units).
 uint32_t pick_chunk_units(uint64_t total_units, int cus) {
     uint64_t target = total_units / (uint64_t(cus) * 8);
-    uint32_t cu = 64;
+    uint32_t cu = 256;
     while (cu > uint32_t(kRows) && cu > target) cu >>= 1;
     return cu;
 }

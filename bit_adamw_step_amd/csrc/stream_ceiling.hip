@@ -3,10 +3,11 @@
 // per quantized value (FP32 weight read and write, BF16 gradient read, 4-bit m and v codes read
 // and write, and per 128-value block the two FP32 scales read and written: 12.125 B per value)
 // with trivial arithmetic, in the step kernel's access pattern: each 256-thread workgroup walks
-// runs of consecutive 128-value blocks, a 16-lane row per block, 8 values per lane.  Its time
-// is the floor any fused step with that byte mix can reach here.  Like the step, it loads the
-// read-once gradients non-temporally (1% faster here); non-temporal weight or code accesses
-// were slower and are not used.
+// runs of consecutive 128-value blocks, a 16-lane row per block, lane r of a row holding the
+// block's values 4r..4r+3 and 64+4r..64+4r+3 (so a row's 16-byte weight accesses cover 256
+// contiguous bytes), its codes two 16-bit pieces 32 bytes apart.  Like the step it streams
+// the weights and gradients non-temporally.  Its time is the floor any fused step with that
+// byte mix can reach here.
 //
 // C entry point (loaded by the benchmark with ctypes):
 //   int adamw4_ceiling_mix(float* w, const uint16_t* g, uint32_t* mcodes, uint32_t* vcodes,
@@ -21,42 +22,54 @@
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void __launch_bounds__(256) ceiling_mix_kernel(float* __restrict__ w,
                                                           const uint16_t* __restrict__ g,
-                                                          uint32_t* __restrict__ mc,
-                                                          uint32_t* __restrict__ vc,
+                                                          uint32_t* __restrict__ mc32,
+                                                          uint32_t* __restrict__ vc32,
                                                           float* __restrict__ sm,
                                                           float* __restrict__ sv, int64_t nblocks,
                                                           int64_t chunk_blocks) {
-    const int64_t lanes = nblocks * 16;                  // one lane = 8 values
+    uint16_t* mc = reinterpret_cast<uint16_t*>(mc32);
+    uint16_t* vc = reinterpret_cast<uint16_t*>(vc32);
+    const int64_t lanes = nblocks * 16;                  // 16 lanes (one row) per block
     const int64_t chunk = chunk_blocks * 16;
     const int64_t nchunks = (lanes + chunk - 1) / chunk;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t end = min(lanes, (c + 1) * chunk);
         for (int64_t i = c * chunk + threadIdx.x; i < end; i += blockDim.x) {
-            float4* wp = reinterpret_cast<float4*>(w) + 2 * i;
-            const uint32_t m = mc[i], v = vc[i];
-            const u32x4 g4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g) + i);
-            const uint4 gg = make_uint4(g4.x, g4.y, g4.z, g4.w);
-            float4 a = wp[0], b = wp[1];
+            const int64_t blk = i >> 4;
+            const int rl = (int)(i & 15);
+            const int64_t q = blk * 32 + rl;             // the lane's first 4-value group
+            f32x4* wp = reinterpret_cast<f32x4*>(w) + q;
+            const u32x2* gp = reinterpret_cast<const u32x2*>(g) + q;
+            const uint32_t m = mc[q] | ((uint32_t)mc[q + 16] << 16);
+            const uint32_t v = vc[q] | ((uint32_t)vc[q + 16] << 16);
+            const u32x2 g0 = __builtin_nontemporal_load(gp);
+            const u32x2 g1 = __builtin_nontemporal_load(gp + 16);
+            f32x4 a = __builtin_nontemporal_load(wp);
+            f32x4 b = __builtin_nontemporal_load(wp + 16);
             float s0 = 0.0f, s1 = 0.0f;
-            if ((i & 15) == 0) {
-                s0 = sm[i >> 4];
-                s1 = sv[i >> 4];
+            if (rl == 0) {
+                s0 = sm[blk];
+                s1 = sv[blk];
             }
-            a.x -= __uint_as_float(gg.x << 16); a.y -= __uint_as_float(gg.x & 0xFFFF0000u);
-            a.z -= __uint_as_float(gg.y << 16); a.w -= __uint_as_float(gg.y & 0xFFFF0000u);
-            b.x -= __uint_as_float(gg.z << 16); b.y -= __uint_as_float(gg.z & 0xFFFF0000u);
-            b.z -= __uint_as_float(gg.w << 16); b.w -= __uint_as_float(gg.w & 0xFFFF0000u);
-            wp[0] = a;
-            wp[1] = b;
-            mc[i] = m ^ 0x11111111u;
-            vc[i] = v ^ 0x22222222u;
-            if ((i & 15) == 0) {
-                sm[i >> 4] = s0 * 0.5f;
-                sv[i >> 4] = s1 * 0.5f;
+            a.x -= __uint_as_float(g0.x << 16); a.y -= __uint_as_float(g0.x & 0xFFFF0000u);
+            a.z -= __uint_as_float(g0.y << 16); a.w -= __uint_as_float(g0.y & 0xFFFF0000u);
+            b.x -= __uint_as_float(g1.x << 16); b.y -= __uint_as_float(g1.x & 0xFFFF0000u);
+            b.z -= __uint_as_float(g1.y << 16); b.w -= __uint_as_float(g1.y & 0xFFFF0000u);
+            __builtin_nontemporal_store(a, wp);
+            __builtin_nontemporal_store(b, wp + 16);
+            const uint32_t nm = m ^ 0x11111111u, nv = v ^ 0x22222222u;
+            mc[q] = (uint16_t)nm;
+            mc[q + 16] = (uint16_t)(nm >> 16);
+            vc[q] = (uint16_t)nv;
+            vc[q + 16] = (uint16_t)(nv >> 16);
+            if (rl == 0) {
+                sm[blk] = s0 * 0.5f;
+                sv[blk] = s1 * 0.5f;
             }
         }
     }
