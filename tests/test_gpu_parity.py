@@ -139,6 +139,45 @@ def test_mixed_list_modes(env):
     print({k: v for k, v in rep.items() if "flips" in k and v})
 
 
+def test_tail_positions_in_the_lane_map(env):
+    """A lane holds slots 4r..4r+3 (half A) and 64+4r..64+4r+3 (half B) of its block, so a
+    partial last block can end inside a lane's half A, exactly at the half boundary, inside half
+    B, or one slot short of full.  Tails at each of those positions (1, 3, 4, 5, 63, 64, 65, 67,
+    68, 124, 127 values), each with 8 full blocks before it, through every v rule, the LM-head
+    switch and FP32 m, with FP32 and BF16 grads; the init encoder and decode on the same list."""
+    A, orc = env
+    rems = [1, 3, 4, 5, 63, 64, 65, 67, 68, 124, 127]
+    sizes = [128 * 40 + r for r in rems]
+    flags = [0, A.T_HEAD, A.T_FP32_M, 0, A.T_HEAD, 0, A.T_FP32_M, 0, A.T_HEAD, 0, A.T_FP32_M]
+    gdt = ["bf16" if i % 2 else "f32" for i in range(len(sizes))]
+    sched = [(1, A.ZIP_SR, -1, 0), (2, A.ZE_EDEN, A.ZIP_SR, 1), (3, A.V_SSR, A.ZE_EDEN, 1),
+             (4, A.V_RTN, A.V_SSR, 0), (5, A.V_PRTN, A.V_RTN, 1), (6, A.V_ZE_RTN, A.V_PRTN, 0),
+             (7, A.ZIP_SR, A.V_ZE_RTN, 1)]
+    rep = _run_steps(env, sizes, flags, gdt, sched, seed=21)
+    assert all(v for k, v in rep.items() if k.endswith("w_bitexact"))
+    # the deterministic init encoder from given moments, then decode, at the same tails
+    import torch
+    from gpu_harness import GpuList, oracle_state, compare_state, to_np, say
+    rng = np.random.default_rng(22)
+    for mode in (A.ZIP_SR, A.ZE_EDEN, A.V_ZE_RTN):
+        gl = GpuList(sizes, flags, ["f32"] * len(sizes))
+        m0 = [rng.normal(0, 1e-3, n).astype(f32) for n in sizes]
+        v0 = [(10 ** rng.uniform(-12, -4, n)).astype(f32) for n in sizes]
+        say(f"init+decode mode={mode} sizes={sizes}")
+        gl.pl.init(mode, [torch.from_numpy(x).cuda() for x in m0],
+                   [torch.from_numpy(x).cuda() for x in v0])
+        _, _, ss = gl.snapshot()
+        crep = {}
+        for i, n in enumerate(sizes):
+            ref = orc.init_state(n, False, mode, m0[i], v0[i], fp32_m=bool(flags[i] & A.T_FP32_M))
+            compare_state(f"init{i}", n, oracle_state(ss[i], n, flags[i]), ref, None, crep)
+            mo = torch.empty(n, device="cuda")
+            vo = torch.empty(n, device="cuda")
+            A.decode_state(gl.pl.array[i], mode, mo.data_ptr(), vo.data_ptr())
+            rm, rv = orc.decode(ref, n, mode)
+            assert np.array_equal(to_np(mo), rm) and np.array_equal(to_np(vo), rv), (mode, n)
+
+
 def test_study_modes(env):
     """The controlled study's other v rules (state-space RTN, state-space SR, preconditioner-
     space RTN) on the ragged mixed list, alone and switching with ZIP-SR and ZE-EDEN (decoding
