@@ -5,8 +5,9 @@
 // with trivial arithmetic, in the step kernel's access pattern: each 256-thread workgroup walks
 // runs of consecutive 128-value blocks, a 16-lane row per block, lane r of a row holding the
 // block's values 4r..4r+3 and 64+4r..64+4r+3 (so a row's 16-byte weight accesses cover 256
-// contiguous bytes), its codes two 16-bit pieces 32 bytes apart.  Like the step it streams
-// the weights and gradients non-temporally.  Its time is the floor any fused step with that
+// contiguous bytes), and each row moving its block's 64 code bytes per array as one dword per
+// lane (lane 2k the dword at byte 4k, lane 2k+1 the one at byte 32 + 4k).  Like the step it
+// streams the weights, gradients and codes non-temporally.  Its time is the floor any fused step with that
 // byte mix can reach here.
 //
 // C entry point (loaded by the benchmark with ctypes):
@@ -32,8 +33,6 @@ __global__ void __launch_bounds__(256) ceiling_mix_kernel(float* __restrict__ w,
                                                           float* __restrict__ sm,
                                                           float* __restrict__ sv, int64_t nblocks,
                                                           int64_t chunk_blocks) {
-    uint16_t* mc = reinterpret_cast<uint16_t*>(mc32);
-    uint16_t* vc = reinterpret_cast<uint16_t*>(vc32);
     const int64_t lanes = nblocks * 16;                  // 16 lanes (one row) per block
     const int64_t chunk = chunk_blocks * 16;
     const int64_t nchunks = (lanes + chunk - 1) / chunk;
@@ -45,8 +44,9 @@ __global__ void __launch_bounds__(256) ceiling_mix_kernel(float* __restrict__ w,
             const int64_t q = blk * 32 + rl;             // the lane's first 4-value group
             f32x4* wp = reinterpret_cast<f32x4*>(w) + q;
             const u32x2* gp = reinterpret_cast<const u32x2*>(g) + q;
-            const uint32_t m = mc[q] | ((uint32_t)mc[q + 16] << 16);
-            const uint32_t v = vc[q] | ((uint32_t)vc[q + 16] << 16);
+            const int64_t cd = blk * 16 + (rl >> 1) + (rl & 1) * 8;   // the lane's code dword
+            const uint32_t m = __builtin_nontemporal_load(mc32 + cd);
+            const uint32_t v = __builtin_nontemporal_load(vc32 + cd);
             const u32x2 g0 = __builtin_nontemporal_load(gp);
             const u32x2 g1 = __builtin_nontemporal_load(gp + 16);
             f32x4 a = __builtin_nontemporal_load(wp);
@@ -63,10 +63,8 @@ __global__ void __launch_bounds__(256) ceiling_mix_kernel(float* __restrict__ w,
             __builtin_nontemporal_store(a, wp);
             __builtin_nontemporal_store(b, wp + 16);
             const uint32_t nm = m ^ 0x11111111u, nv = v ^ 0x22222222u;
-            mc[q] = (uint16_t)nm;
-            mc[q + 16] = (uint16_t)(nm >> 16);
-            vc[q] = (uint16_t)nv;
-            vc[q + 16] = (uint16_t)(nv >> 16);
+            __builtin_nontemporal_store(nm, mc32 + cd);
+            __builtin_nontemporal_store(nv, vc32 + cd);
             if (rl == 0) {
                 sm[blk] = s0 * 0.5f;
                 sv[blk] = s1 * 0.5f;
