@@ -252,7 +252,7 @@ def ceiling(q: int, device, reps: int = 5) -> dict | None:
     del wv, g, mc, vc, sm, sv
     torch.cuda.empty_cache()
     return {"kernel": "same-byte-mix streaming (12.125 B/value, step access pattern, "
-                      "non-temporal weights and grads)",
+                      "non-temporal weights, grads and codes)",
             "values": n, "ms": round(ms, 4), "GBs": round(byts / (ms / 1000) / 1e9, 1),
             "grid": grid, "chunk_blocks": chunk}
 
