@@ -14,7 +14,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <functional>
 #include <mutex>
+#include <queue>
 #include <vector>
 
 #include "../../include/adamw4.h"
@@ -160,7 +162,6 @@ struct Plan {
     int device = -1;
     std::vector<TensorDesc> descs;  // host copy, also the cache key
     uint32_t nchunks = 0;
-    uint32_t chunk_units = 0;
     uint32_t ntails = 0;
     bool extra = false;             // some tensor has a BF16 copy or a shard offset
     size_t tails_off = 0;           // byte offset of the tail list in dbuf
@@ -196,10 +197,11 @@ adamw4_status device_info(int dev, DeviceInfo& out) {
 }
 
 // Chunk size: 256 units (32768 values) for large lists, so each workgroup streams long runs
-// of consecutive lines; smaller when the list is too small to give every CU several chunks,
-// but never below one workgroup iteration (16 units).
-uint32_t pick_chunk_units(uint64_t total_units, int cus) {
-    uint64_t target = total_units / (uint64_t(cus) * 8);
+// of consecutive lines; smaller when the list is too small to give each of the launch's
+// workgroups about 8 chunks (so the last round of chunks leaves little idle time), but never
+// below one workgroup iteration (16 units).
+uint32_t pick_chunk_units(uint64_t total_units, int workgroups) {
+    uint64_t target = total_units / (uint64_t(workgroups) * 8);
     uint32_t cu = 256;
     while (cu > uint32_t(kRows) && cu > target) cu >>= 1;
     return cu;
@@ -212,8 +214,78 @@ uint64_t plan_units(const TensorDesc& d, bool split_tails) {
     return uint64_t((d.numel + kBlock - 1) / kBlock);
 }
 
+// The launch walks the chunk table with a grid stride: workgroup w takes entries w, w + G,
+// w + 2G, ... (G workgroups), so the workgroups stream neighbouring chunks together (giving
+// each workgroup one contiguous range of the list instead was 6% slower in the streaming
+// probe).  The table is laid out so that this order is balanced:
+//   1. the last partial round of chunks and the full round before it are re-cut, in list
+//      order, into about 4 G pieces of (nearly) equal length in whole workgroup iterations, so
+//      the launch ends on small pieces;
+//   2. chunks are dealt in list order, each to the workgroup with the least work so far
+//      (ceil(units / 16) iterations; ties to the lowest index, which is round-robin when the
+//      chunks are equal);
+//   3. workgroup w's k-th chunk is stored at entry k G + w; workgroups with fewer chunks get
+//      empty entries (units = 0).
+// Left alone when the list has at most G chunks.
+void balance_chunks(std::vector<Chunk>& chunks, uint64_t workgroups) {
+    const uint64_t n = chunks.size();
+    const uint64_t G = workgroups;
+    if (G < 2 || n <= G) return;
+    // 1. re-cut the tail
+    if (n % G != 0) {
+        const uint64_t t0 = n - G - n % G;   // first re-cut chunk
+        uint64_t total = 0;
+        for (uint64_t i = t0; i < n; ++i) total += chunks[i].units;
+        const uint64_t pieces = 4 * G;
+        // end of piece j in the re-cut stretch: j * total / pieces rounded to a multiple of kRows
+        auto cut = [&](uint64_t j) -> uint64_t {
+            if (j >= pieces) return total;
+            return std::min<uint64_t>(total, (j * total / pieces + kRows / 2) / kRows * kRows);
+        };
+        std::vector<Chunk> out(chunks.begin(), chunks.begin() + t0);
+        uint64_t pos = 0, j = 1;
+        for (uint64_t i = t0; i < n;) {
+            // a run of contiguous chunks of one tensor
+            Chunk run = chunks[i++];
+            while (i < n && chunks[i].tensor == run.tensor &&
+                   chunks[i].first_unit == run.first_unit + run.units)
+                run.units += chunks[i++].units;
+            const uint64_t end = pos + run.units;
+            for (uint64_t cur = pos; cur < end;) {
+                while (cut(j) <= cur) ++j;
+                const uint64_t stop = std::min(cut(j), end);
+                out.push_back(Chunk{run.tensor, uint32_t(run.first_unit + (cur - pos)),
+                                    uint32_t(stop - cur), 0});
+                cur = stop;
+            }
+            pos = end;
+        }
+        chunks.swap(out);
+    }
+    // 2. deal to the least-loaded workgroup
+    using Load = std::pair<uint64_t, uint64_t>;   // (iterations so far, workgroup)
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (uint64_t w = 0; w < G; ++w) heap.push(Load{0, w});
+    std::vector<std::vector<uint32_t>> mine(G);
+    for (uint64_t c = 0; c < chunks.size(); ++c) {
+        Load l = heap.top();
+        heap.pop();
+        mine[l.second].push_back(uint32_t(c));
+        l.first += (chunks[c].units + kRows - 1) / kRows;
+        heap.push(l);
+    }
+    // 3. lay out the rounds
+    size_t rounds = 0;
+    for (const auto& m : mine) rounds = std::max(rounds, m.size());
+    std::vector<Chunk> table(rounds * G, Chunk{0, 0, 0, 0});
+    for (uint64_t w = 0; w < G; ++w)
+        for (size_t k = 0; k < mine[w].size(); ++k) table[k * G + w] = chunks[mine[w][k]];
+    chunks.swap(table);
+}
+
+
 // Build descriptor, chunk and tail tables and copy them to a fresh device buffer.
-adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool split_tails,
+adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int workgroups, bool split_tails,
                          Plan*& out) {
     uint64_t total_units = 0;
     for (const TensorDesc& d : descs) {
@@ -221,7 +293,7 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool
         if (plan_units(d, split_tails) > uint64_t(UINT32_MAX)) return ADAMW4_ESIZE;
         total_units += plan_units(d, split_tails);
     }
-    const uint32_t cu = pick_chunk_units(total_units, cus);
+    const uint32_t cu = pick_chunk_units(total_units, workgroups);
     std::vector<Chunk> chunks;
     std::vector<uint32_t> tails;
     uint64_t nch = 0;
@@ -230,10 +302,13 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool
     chunks.reserve(size_t(nch));
     for (size_t i = 0; i < descs.size(); ++i) {
         const uint64_t units = plan_units(descs[i], split_tails);
-        for (uint64_t u = 0; u < units; u += cu) chunks.push_back(Chunk{uint32_t(i), uint32_t(u)});
+        for (uint64_t u = 0; u < units; u += cu)
+            chunks.push_back(Chunk{uint32_t(i), uint32_t(u), uint32_t(std::min<uint64_t>(cu, units - u)), 0});
         if (split_tails && (descs[i].flags & D_QUANT) && descs[i].numel % kBlock != 0)
             tails.push_back(uint32_t(i));
     }
+    balance_chunks(chunks, uint64_t(workgroups));
+    if (chunks.size() > UINT32_MAX) return ADAMW4_ESIZE;
     const size_t dbytes = align16(descs.size() * sizeof(TensorDesc));
     const size_t cbytes = align16(chunks.size() * sizeof(Chunk));
     const size_t bytes = dbytes + cbytes + tails.size() * sizeof(uint32_t);
@@ -252,7 +327,6 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int cus, bool
     p->device = dev;
     p->descs = std::move(descs);
     p->nchunks = uint32_t(chunks.size());
-    p->chunk_units = cu;
     p->ntails = uint32_t(tails.size());
     for (const TensorDesc& d : p->descs) p->extra = p->extra || d.wcopy != nullptr || d.base != 0;
     p->tails_off = dbytes + cbytes;
@@ -272,7 +346,6 @@ Launch launch_of(const Plan& p, int grid_cap) {
     L.chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(p.dbuf) +
                                               align16(p.descs.size() * sizeof(TensorDesc)));
     L.nchunks = p.nchunks;
-    L.chunk_units = p.chunk_units;
     L.grid = int(std::min<uint64_t>(p.nchunks, uint64_t(std::max(grid_cap, 1))));
     L.tails = reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.dbuf) + p.tails_off);
     L.ntails = p.ntails;
@@ -283,7 +356,7 @@ Launch launch_of(const Plan& p, int grid_cap) {
 // Find or create the cached plan for this descriptor list (the common case in training: the
 // same buffers every step, so the tables are uploaded once).  Evicting a plan waits for the
 // device so no in-flight launch still reads it.
-adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan*& out) {
+adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int workgroups, Plan*& out) {
     for (Plan* p : g_plans) {
         if (p->device == dev && p->descs.size() == descs.size() &&
             std::memcmp(p->descs.data(), descs.data(), descs.size() * sizeof(TensorDesc)) == 0) {
@@ -293,7 +366,7 @@ adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int cus, Plan*&
         }
     }
     Plan* p = nullptr;
-    adamw4_status s = build_plan(std::move(descs), dev, cus, true, p);
+    adamw4_status s = build_plan(std::move(descs), dev, workgroups, true, p);
     if (s != ADAMW4_OK) return s;
     if (g_plans.size() >= size_t(kMaxPlans)) {
         auto lru = std::min_element(g_plans.begin(), g_plans.end(),
@@ -358,7 +431,7 @@ adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hpara
     DeviceInfo di;
     if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
     Plan* p = nullptr;
-    if ((s = get_plan(std::move(descs), dev, di.cus, p)) != ADAMW4_OK) return s;
+    if ((s = get_plan(std::move(descs), dev, di.cus * di.step_bpc, p)) != ADAMW4_OK) return s;
     const Launch L = launch_of(*p, di.cus * di.step_bpc);
     if (launch_step(L, a, static_cast<hipStream_t>(stream)) != hipSuccess) return ADAMW4_EHIP;
     return ADAMW4_OK;
@@ -374,7 +447,7 @@ static adamw4_status run_aux(std::vector<TensorDesc>&& descs, bool init, int32_t
     DeviceInfo di;
     if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
     Plan* p = nullptr;
-    if ((s = build_plan(std::move(descs), dev, di.cus, false, p)) != ADAMW4_OK) return s;
+    if ((s = build_plan(std::move(descs), dev, di.cus * di.aux_bpc, false, p)) != ADAMW4_OK) return s;
     const Launch L = launch_of(*p, di.cus * di.aux_bpc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = init ? launch_init(L, mode, st) : launch_decode(L, mode, st);

@@ -37,10 +37,12 @@ struct alignas(16) TensorDesc {
     uint32_t pos;      // the tensor's RNG key
 };
 
-// A run of up to `chunk_units` consecutive 128-value units of one tensor.
-struct Chunk {
+// A run of `units` consecutive 128-value units of one tensor, from `first_unit` on.
+struct alignas(16) Chunk {
     uint32_t tensor;
     uint32_t first_unit;
+    uint32_t units;
+    uint32_t reserved;
 };
 
 // Per-step scalars, formed on the host in binary64 and rounded once to FP32.
@@ -62,7 +64,6 @@ struct Launch {
     const TensorDesc* descs;   // device
     const Chunk* chunks;       // device
     uint32_t nchunks;
-    uint32_t chunk_units;
     int grid;
     // Step launches only: quantized tensors whose last 128-value block is partial.  Their full
     // blocks are in the chunk table; the partial blocks go to a second, small launch so the

@@ -178,6 +178,24 @@ def test_tail_positions_in_the_lane_map(env):
             assert np.array_equal(to_np(mo), rm) and np.array_equal(to_np(vo), rv), (mode, n)
 
 
+def test_balanced_last_rounds(env):
+    """Lists with more chunks than the launch has workgroups: the plan deals chunks round-robin
+    and re-cuts the last partial round and the round before it into two pieces per workgroup
+    (the whole list in the first case here, its second half in the second, across tensor
+    boundaries, ragged tails and FP32-state tensors).  Every value of every tensor is compared
+    with the oracle, so a unit stepped twice or not at all fails."""
+    A = env[0]
+    sizes = [65536] * 40 + [65536 + 77, 3000, 4096 * 3 + 5, 200000 + 33]
+    flags = [0] * 40 + [A.T_HEAD, 0, A.T_FP32_M, 0]
+    gdt = ["bf16"] * 20 + ["f32"] * 20 + ["bf16", "f32", "bf16", "f32"]
+    _run_steps(env, sizes, flags, gdt, [(1, A.ZIP_SR, -1, 1), (2, A.ZE_EDEN, A.ZIP_SR, 0)],
+               seed=31)
+    sizes = [1 << 20] * 6 + [300000 + 17, 5000, 2000, 128 * 700 + 1]
+    flags = [0, A.T_FP32_M, 0, 0, A.T_HEAD, 0, 0, A.T_NORM, 0, 0]
+    gdt = ["bf16", "f32"] * 5
+    _run_steps(env, sizes, flags, gdt, [(1, A.ZIP_SR, -1, 0), (2, A.V_SSR, A.ZIP_SR, 1)], seed=32)
+
+
 def test_study_modes(env):
     """The controlled study's other v rules (state-space RTN, state-space SR, preconditioner-
     space RTN) on the ragged mixed list, alone and switching with ZIP-SR and ZE-EDEN (decoding
