@@ -160,6 +160,7 @@ TensorDesc make_desc(const adamw4_tensor& t, uint32_t pos) {
 // Device memory for one launch's descriptors and chunk table.
 struct Plan {
     int device = -1;
+    int workgroups = 0;             // the launch grid the chunk table is dealt for
     std::vector<TensorDesc> descs;  // host copy, also the cache key
     uint32_t nchunks = 0;
     uint32_t ntails = 0;
@@ -171,7 +172,7 @@ struct Plan {
 
 struct DeviceInfo {
     int cus = 0;
-    int step_bpc = 0;
+    int step_bpc[6] = {0, 0, 0, 0, 0, 0};   // per v rule (adamw4_mode)
     int aux_bpc = 0;
 };
 
@@ -189,7 +190,7 @@ adamw4_status device_info(int dev, DeviceInfo& out) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return ADAMW4_EHIP;
         di.cus = std::max(cus, 1);
-        di.step_bpc = step_blocks_per_cu();
+        for (int m = 0; m < 6; ++m) di.step_bpc[m] = step_blocks_per_cu(m);
         di.aux_bpc = aux_blocks_per_cu();
     }
     out = di;
@@ -325,6 +326,7 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int workgroup
     }
     Plan* p = new Plan;
     p->device = dev;
+    p->workgroups = workgroups;
     p->descs = std::move(descs);
     p->nchunks = uint32_t(chunks.size());
     p->ntails = uint32_t(tails.size());
@@ -358,7 +360,7 @@ Launch launch_of(const Plan& p, int grid_cap) {
 // device so no in-flight launch still reads it.
 adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int workgroups, Plan*& out) {
     for (Plan* p : g_plans) {
-        if (p->device == dev && p->descs.size() == descs.size() &&
+        if (p->device == dev && p->workgroups == workgroups && p->descs.size() == descs.size() &&
             std::memcmp(p->descs.data(), descs.data(), descs.size() * sizeof(TensorDesc)) == 0) {
             p->last_use = ++g_clock;
             out = p;
@@ -431,8 +433,9 @@ adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hpara
     DeviceInfo di;
     if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
     Plan* p = nullptr;
-    if ((s = get_plan(std::move(descs), dev, di.cus * di.step_bpc, p)) != ADAMW4_OK) return s;
-    const Launch L = launch_of(*p, di.cus * di.step_bpc);
+    const int grid = di.cus * di.step_bpc[hp->mode];
+    if ((s = get_plan(std::move(descs), dev, grid, p)) != ADAMW4_OK) return s;
+    const Launch L = launch_of(*p, grid);
     if (launch_step(L, a, static_cast<hipStream_t>(stream)) != hipSuccess) return ADAMW4_EHIP;
     return ADAMW4_OK;
 }

@@ -78,7 +78,7 @@ hipError_t launch_init(const Launch& L, int32_t mode, hipStream_t s);
 hipError_t launch_decode(const Launch& L, int32_t mode, hipStream_t s);
 
 // Resident workgroups per CU of each kernel on the current device (for persistent grids).
-int step_blocks_per_cu();
+int step_blocks_per_cu(int mode);   // workgroups per CU of the step launch for a v rule
 int aux_blocks_per_cu();
 
 // Host copies of the compiled-in codebooks (0 NF4, 1 V0, 2 V1).
