@@ -5,11 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "chunk_plan.h"
+
 namespace adamw4 {
 
 constexpr int kBlock = 128;              // values per FP32 block scale
 constexpr int kLanes = 16;               // lanes that share one 128-value block (a DPP row)
-constexpr int kPerLane = 8;              // consecutive values held by one lane
+constexpr int kPerLane = 8;              // values held by one lane (two runs of 4 in the step)
 constexpr int kWG = 256;                 // threads per workgroup (4 waves of 64)
 constexpr int kRows = kWG / kLanes;      // blocks processed per workgroup iteration
 constexpr int kMinQuant = 4096;          // smaller tensors keep FP32 moments
@@ -37,13 +39,7 @@ struct alignas(16) TensorDesc {
     uint32_t pos;      // the tensor's RNG key
 };
 
-// A run of `units` consecutive 128-value units of one tensor, from `first_unit` on.
-struct alignas(16) Chunk {
-    uint32_t tensor;
-    uint32_t first_unit;
-    uint32_t units;
-    uint32_t reserved;
-};
+static_assert(kRows == kPlanRows, "the chunk plan counts workgroup iterations of kRows blocks");
 
 // Per-step scalars, formed on the host in binary64 and rounded once to FP32.
 struct StepArgs {
