@@ -54,7 +54,7 @@ typedef enum {
  * V_SSR, state-space stochastic rounding (lower level with probability (b-v)/(b-a)); V_PRTN,
  * preconditioner-space round to nearest (the level with the nearest h, ties low).
  * V_ZE_RTN is the baseline the pages measure against ([lav-ZE]: TorchAO's positive floor;
- * [lav-ST]: a small positive bottom notch): the zero-excluding codebook, nearest level, the
+ * [lav-ST]: a positive lowest level): the zero-excluding codebook, nearest level, the
  * plain absmax block scale -- ZE-EDEN without its rescale.  A v encoded by ZE-EDEN or V_ZE_RTN
  * decodes with the zero-excluding codebook, by any other mode with the zero-inclusive one. */
 typedef enum {

@@ -126,8 +126,8 @@ static void v0_table(float out[16]) {
     for (int k = 0; k < 16; ++k) out[k] = (float)((double)k / 15.0);
 }
 
-/* Zero-excluding v codebook for ZE-EDEN: (k+1)/16, bottom notch 1/16 ([lav-ST]: the bottom
- * notch is a small positive number; [lav-ZE]: TorchAO's positive floor is kept). */
+/* Zero-excluding v codebook for ZE-EDEN: (k+1)/16, lowest level 1/16 ([lav-ST]: the
+ * zero-free codebook's lowest level is positive; [lav-ZE]: TorchAO's positive floor is kept). */
 static void v1_table(float out[16]) {
     for (int k = 0; k < 16; ++k) out[k] = (float)(k + 1) / 16.0f;
 }

@@ -6,6 +6,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+# The mutation tests run the pin suite against a planted-mistake copy of the oracle package.
+if os.environ.get("ADAMW4_ORACLE_PKG"):
+    sys.path.insert(0, os.environ["ADAMW4_ORACLE_PKG"])
 
 
 def pytest_configure(config):

@@ -1,6 +1,8 @@
 """The oracle's pins must catch plausible mistakes: each case below plants one error in a
 copy of the oracle source (on the CPU only), builds it, and runs the pin suite against it; the
-suite must fail.  The unmodified source must pass (checked by the pin suite itself)."""
+suite must fail.  The unmodified source must pass (checked by the pin suite itself).  C mutants
+change adamw4_oracle.c; the PY_MUTANTS change the oracle's Python wrapper (its per-tensor state
+handling), run from a copy of the oracle package placed first on the import path."""
 import os
 import subprocess
 import sys
@@ -58,6 +60,24 @@ MUTANTS = {
                           "case ORC_V_ZE_RTN: encode_v_eden_block(vw, V1, cv, vscale); break;"),
     "baseline_decodes_v0": ("static int uses_v1(int mode) { return mode == ORC_ZE_EDEN || mode == ORC_V_ZE_RTN; }",
                             "static int uses_v1(int mode) { return mode == ORC_ZE_EDEN; }"),
+    # the initial-state encoder
+    "init_eden_no_gamma": ("        if (mode == ORC_ZE_EDEN) encode_v_eden_block(vw, V1, cv, &vscale[b]);",
+                           "        if (0) encode_v_eden_block(vw, V1, cv, &vscale[b]);"),
+    "init_eden_on_v0": ("        if (mode == ORC_ZE_EDEN) encode_v_eden_block(vw, V1, cv, &vscale[b]);",
+                        "        if (mode == ORC_ZE_EDEN) encode_v_eden_block(vw, V0, cv, &vscale[b]);"),
+    "init_baseline_on_v0": ("        else encode_v_rtn_block(vw, uses_v1(mode) ? V1 : V0, cv, &vscale[b]);",
+                            "        else encode_v_rtn_block(vw, V0, cv, &vscale[b]);"),
+    "init_m_stochastic": ("        encode_m_block(mw, nvalid, 0, NF4, 0, 0, 0, 0, cm, &mscale[b], NULL);",
+                          "        encode_m_block(mw, nvalid, 1, NF4, 0, 0, 0, 0, cm, &mscale[b], NULL);"),
+}
+
+PY_MUTANTS = {
+    "init_fp32m_drops_m0": ("        m = np.zeros(n, np.float32) if m0 is None else np.asarray(m0, np.float32).copy()\n"
+                            "        return State(True, None, full.vcodes",
+                            "        m = np.zeros(n, np.float32)\n"
+                            "        return State(True, None, full.vcodes"),
+    "init_fp32m_ignores_v0": ("        full = init_state(n, norm, mode, None, v0)",
+                              "        full = init_state(n, norm, mode, None, None)"),
 }
 
 
@@ -72,6 +92,22 @@ def test_pins_catch_mutant(name, tmp_path):
     subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
                     "-o", str(lib), str(mut), "-lm"], check=True, capture_output=True)
     env = dict(os.environ, ADAMW4_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode != 0, f"pin suite passed with mutant {name}:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_catch_wrapper_mutant(name, tmp_path):
+    old, new = PY_MUTANTS[name]
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    (pkg / "__init__.py").write_text(src.replace(old, new))
+    (pkg / "adamw4_oracle.c").write_text(open(SRC).read())
+    env = dict(os.environ, ADAMW4_ORACLE_PKG=str(tmp_path))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        env=env, capture_output=True, text=True, cwd=ROOT)

@@ -44,7 +44,7 @@ def test_nf4_matches_scipy_quantile_construction(orc):
 
 
 def test_v_codebooks(orc):
-    """ZIP-SR keeps zero in the v codebook, ZE-EDEN's bottom notch is positive ([kc-TC], [lav-ST])."""
+    """ZIP-SR keeps zero in the v codebook, ZE-EDEN's lowest level is positive ([kc-TC], [lav-ST])."""
     from fractions import Fraction
     v0 = orc.codebook(orc.CB_V0)
     v1 = orc.codebook(orc.CB_V1)
@@ -586,8 +586,8 @@ def test_eden_no_zero_and_scale_closed_form(orc):
 # ---------------------------------------------------------------------------------------------
 
 def test_baseline_is_eden_without_rescale(orc):
-    """The baseline keeps the positive floor ([lav-ZE]: TorchAO's; [lav-ST]: the bottom notch
-    is a small positive number), so no value of a non-zero block decodes to zero; it takes the
+    """The baseline keeps the positive floor ([lav-ZE]: TorchAO's; [lav-ST]: its codebook's lowest
+    level is positive), so no value of a non-zero block decodes to zero; it takes the
     same nearest V1 codes as ZE-EDEN ([kc-TC]: ZE-EDEN = zero removal + block rescale) and
     stores the plain absmax, which ZE-EDEN multiplies by gamma."""
     V1 = orc.codebook(orc.CB_V1)
@@ -834,3 +834,120 @@ def test_bf16_grads_widen_exactly(orc):
     orc.step_tensor(wa, gbf, sa, orc.HParams(step=1), pos=0)
     orc.step_tensor(wb, gw, sb, orc.HParams(step=1), pos=0)
     assert np.array_equal(wa, wb) and np.array_equal(sa.vcodes, sb.vcodes)
+
+
+# ---------------------------------------------------------------------------------------------
+# P-16  the initial-state encoder (no page defines one; the reading is a deterministic nearest
+# level with the pages' block format, plus ZE-EDEN's rescale): each block recomputed here by
+# brute force over the 16 levels and the rescale's closed form in binary64
+# ---------------------------------------------------------------------------------------------
+
+def _unpack(codes, n):
+    return np.stack([codes & 15, codes >> 4], 1).reshape(-1)[:n]
+
+
+def _init_inputs(seed, n):
+    """m0 ~ N(0, 1e-3) with 10% exact zeros and one all-zero block; v0 log-uniform in
+    [1e-20, 1e-4] (the pre-seeded v of the 834M list) with its own all-zero block; the last block
+    is partial."""
+    rng = np.random.default_rng(seed)
+    m0 = rng.normal(0, 1e-3, n).astype(f32)
+    m0[rng.random(n) < 0.1] = 0
+    m0[128:256] = 0
+    v0 = (10 ** rng.uniform(-20, -4, n)).astype(f32)
+    v0[256:384] = 0
+    v0[rng.random(n) < 0.05] = 0
+    return m0, v0
+
+
+def _nearest_low(y, C):
+    """Index of the nearest level, a tie going to the lower one (argmin keeps the first)."""
+    return np.abs(y.astype(np.float64)[:, None] - C.astype(np.float64)[None, :]).argmin(1)
+
+
+def _check_near(codes, y, C, what):
+    """codes equal the binary64 nearest level, except where y lies within two FP32 ulps of a
+    midpoint (the encoder's own FP32 midpoint then decides), which must be rare."""
+    best = _nearest_low(y, C)
+    bad = np.nonzero(best != codes)[0]
+    for j in bad:
+        k0, k1 = sorted((int(best[j]), int(codes[j])))
+        assert k1 - k0 == 1, (what, j)
+        mid = 0.5 * (float(C[k0]) + float(C[k1]))
+        assert abs(float(y[j]) - mid) <= 2 * np.spacing(f32(mid)), (what, j, y[j], mid)
+    assert bad.size <= 2, (what, bad.size)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
+def test_init_encoder_brute_force(orc, mode):
+    """Initial states from given moments: per 128-value block (zero-padded), the m scale is
+    max|m0| ([lav-ST]: one FP32 scale per 128 values) and each m code the nearest NF4 level of
+    m0/scale; the v scale is max v0 and each v code the nearest level of the mode's codebook
+    (zero-free V1 for ZE-EDEN and the baseline, V0 otherwise); ZE-EDEN then multiplies the v
+    scale by gamma = |y|^2 / max(<y, V1[c]>, 1e-12) ([daiwk-CE]).  All-zero blocks store code 7
+    (NF4's zero) / code 0 with scale 0."""
+    n = 128 * 40 + 45
+    m0, v0 = _init_inputs(70 + mode, n)
+    st = orc.init_state(n, False, mode, m0, v0)
+    NF4 = orc.codebook(orc.CB_NF4)
+    V = orc.codebook(orc.CB_V1 if mode in (orc.ZE_EDEN, orc.V_ZE_RTN) else orc.CB_V0)
+    mc, vc = _unpack(st.mcodes, n), _unpack(st.vcodes, n)
+    for b in range((n + 127) // 128):
+        lo, hi = 128 * b, min(n, 128 * b + 128)
+        xm, xv = m0[lo:hi], v0[lo:hi]
+        sm, sv = np.abs(xm).max(), xv.max()
+        assert st.mscale[b] == sm
+        if sm == 0:
+            assert np.all(mc[lo:hi] == 7)
+        else:
+            _check_near(mc[lo:hi], xm * (f32(1) / sm), NF4, ("m", b))
+        if sv == 0:
+            assert np.all(vc[lo:hi] == 0) and st.vscale[b] == 0
+            continue
+        y = xv * (f32(1) / sv)
+        _check_near(vc[lo:hi], y, V, ("v", b))
+        if mode == orc.ZE_EDEN:
+            yd = y.astype(np.float64)
+            q = V[vc[lo:hi]].astype(np.float64)
+            gamma = (yd @ yd) / max(yd @ q, 1e-12)
+            assert abs(st.vscale[b] - gamma * float(sv)) <= 24 * 2**-24 * gamma * float(sv), b
+            assert yd @ q >= 1 - 1e-6       # the block's maximum maps to the top level
+        else:
+            assert st.vscale[b] == sv
+        if mode in (orc.ZE_EDEN, orc.V_ZE_RTN):
+            assert np.all(V[vc[lo:hi]] * st.vscale[b] > 0)   # no decoded zero
+    # the pad nibble of the odd last byte is zero
+    assert st.mcodes[-1] >> 4 == 0 and st.vcodes[-1] >> 4 == 0
+
+
+def test_init_encoder_uses_no_randomness(orc):
+    """No step t exists before the first step, so the initial encoding is deterministic: it is
+    the same whatever the mode's RNG would draw, and a tie between two levels goes low."""
+    NF4 = orc.codebook(orc.CB_NF4)
+    V0 = orc.codebook(orc.CB_V0)
+    n = 4096
+    m0 = np.zeros(n, f32)
+    v0 = np.zeros(n, f32)
+    m0[0], v0[0] = 1.0, 1.0
+    for k in range(15):   # exact FP32 midpoints of adjacent levels
+        m0[1 + k] = f32(0.5) * (NF4[k] + NF4[k + 1])
+        v0[1 + k] = f32(0.5) * (V0[k] + V0[k + 1])
+    a = orc.init_state(n, False, orc.ZIP_SR, m0, v0)
+    b = orc.init_state(n, False, orc.V_SSR, m0, v0)
+    assert np.array_equal(a.mcodes, b.mcodes) and np.array_equal(a.vcodes, b.vcodes)
+    assert _unpack(a.mcodes, n)[1:16].tolist() == list(range(15))
+    assert _unpack(a.vcodes, n)[1:16].tolist() == list(range(15))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 5])
+def test_init_encoder_fp32_m(orc, mode):
+    """A tensor with FP32 first moments ([lav-RO]) stores m0 bit for bit and encodes v exactly as
+    the fully quantized tensor does."""
+    n = 128 * 40 + 9
+    m0, v0 = _init_inputs(90 + mode, n)
+    st = orc.init_state(n, False, mode, m0, v0, fp32_m=True)
+    full = orc.init_state(n, False, mode, m0, v0)
+    assert st.fp32_m and np.array_equal(st.m.view(np.uint32), m0.view(np.uint32))
+    assert np.array_equal(st.vcodes, full.vcodes) and np.array_equal(st.vscale, full.vscale)
+    m_dec, _ = orc.decode(st, n, mode)
+    assert np.array_equal(m_dec.view(np.uint32), m0.view(np.uint32))
