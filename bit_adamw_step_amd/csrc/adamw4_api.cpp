@@ -98,7 +98,9 @@ adamw4_status check_hparams(const adamw4_hparams& h) {
     if (h.step < 1 || h.step > int64_t(UINT32_MAX)) return ADAMW4_EINVAL;
     if (!(h.beta1 >= 0.0f && h.beta1 < 1.0f)) return ADAMW4_EINVAL;
     if (!(h.beta2 >= 0.0f && h.beta2 < 1.0f)) return ADAMW4_EINVAL;
-    if (!(h.eps >= FLT_MIN) || !finite(h.eps)) return ADAMW4_EINVAL;   // a normal float
+    // a normal float no larger than 2^64: with sqrt(v') < 2^64 and 1/sqrt(1-beta2^t) <= 2^12
+    // the update's denominator stays inside [2^-126, 2^77], where the kernel's division is exact
+    if (!(h.eps >= FLT_MIN) || !(h.eps <= 0x1p64f)) return ADAMW4_EINVAL;
     if (!finite(h.lr) || !finite(h.weight_decay)) return ADAMW4_EINVAL;
     if (!valid_mode(h.mode)) return ADAMW4_EINVAL;
     if (h.prev_mode != -1 && !valid_mode(h.prev_mode)) return ADAMW4_EINVAL;

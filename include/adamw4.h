@@ -24,6 +24,10 @@
  *     on the same stream.  The device is the caller's current HIP device.
  *   - Argument errors are detected on the host before anything is enqueued, and nothing is
  *     written when a call returns an error.
+ *   - Gradients, weights and states must be finite.  Device data is not validated: a
+ *     non-finite value, or a gradient whose square (1-beta2) g^2 overflows FP32, leaves that
+ *     block's weights, codes and scales unspecified (no access outside the caller's buffers).
+ *     For finite data every stored bit is the documented function of the inputs.
  */
 #ifndef ADAMW4_H
 #define ADAMW4_H
@@ -126,7 +130,7 @@ typedef struct {
     int64_t step;        /* t >= 1: the step being taken (bias corrections, RNG counter) */
     float lr;            /* finite */
     float beta1, beta2;  /* each in [0, 1) */
-    float eps;           /* a normal float: >= FLT_MIN (2^-126), finite */
+    float eps;           /* a normal float in [FLT_MIN (2^-126), 2^64] */
     float weight_decay;  /* finite; decoupled: w <- (1 - lr*wd) w - ... */
     int32_t mode;        /* adamw4_mode used to encode v this step */
     int32_t prev_mode;   /* adamw4_mode whose codebook encoded the incoming v; -1 = same as mode */
@@ -156,11 +160,14 @@ adamw4_status adamw4_codebook(int32_t which, float out[16]);
 
 /* Write the initial state of n tensors.  m0[i] / v0[i] are device pointers to numel FP32
  * initial moments of tensor i (16-B aligned); a NULL array or a NULL entry means zeros.
- * Non-zero moments are encoded deterministically (absmax scale, nearest level of NF4 for m and
- * of the codebook of `mode` for v, the zero-excluding one for ZE-EDEN and V_ZE_RTN, else the
- * zero-inclusive one; ZE-EDEN adds its block rescale); no RNG is used because no
- * step t exists yet.  Only ts[i].numel, flags, state and state_size are used.  m0 and v0 are
- * host arrays of n pointers.  The call waits for its work on `stream` before returning. */
+ * No page defines an initial encoding of non-zero moments; this library reads it as the
+ * pages' block format ([lav-ST], [daiwk-LR]) filled deterministically: absmax scale, nearest
+ * level of NF4 for m and of the codebook of `mode` for v (the zero-excluding one for ZE-EDEN and
+ * V_ZE_RTN, else the zero-inclusive one), a tie going to the lower level, and ZE-EDEN's block
+ * rescale ([daiwk-CE]); no RNG is used because no step t exists yet.  Tensors with
+ * ADAMW4_T_FP32_M store m0 as given.  Only ts[i].numel, flags, state and state_size are used.
+ * m0 and v0 are host arrays of n pointers.  The call waits for its work on `stream` before
+ * returning; it allocates a small temporary device table. */
 adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode,
                                 const float* const* m0, const float* const* v0, void* stream);
 
@@ -179,13 +186,16 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
 adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
                           void* stream);
 
-/* Decode one tensor's state into FP32 moments (test and checkpoint aid): m_out, v_out are
- * device arrays of t->numel floats, 16-B aligned (either may be NULL).  `mode` names the
- * codebook that encoded v (the last step's mode).  Waits for its work on `stream`. */
+/* Decode one tensor's state into FP32 moments: the decode stage that opens each step in
+ * [daiwk-PM]'s flowchart, m = NF4[code] s_m and v = V[code] s_v, written out (test and
+ * checkpoint aid).  m_out, v_out are device arrays of t->numel floats, 16-B aligned (either
+ * may be NULL); FP32-state tensors are copied.  `mode` names the codebook that encoded v (the
+ * last step's mode).  Waits for its work on `stream`. */
 adamw4_status adamw4_decode_state(const adamw4_tensor* t, int32_t mode, float* m_out,
                                   float* v_out, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (library plumbing; no page defines it).  Never NULL;
+ * unknown codes give "unknown status". */
 const char* adamw4_status_string(int32_t status);
 
 #ifdef __cplusplus

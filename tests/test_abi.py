@@ -147,6 +147,7 @@ cases = [
   ("beta2 -0.1", step([T()], A.hparams(step=1, beta2=-0.1)), EINVAL),
   ("eps 0", step([T()], A.hparams(step=1, eps=0.0)), EINVAL),
   ("eps subnormal", step([T()], A.hparams(step=1, eps=1e-39)), EINVAL),
+  ("eps above 2^64", step([T()], A.hparams(step=1, eps=2.0**64 * 1.0000001)), EINVAL),
   ("lr nan", step([T()], A.hparams(step=1, lr=float("nan"))), EINVAL),
   ("wd inf", step([T()], A.hparams(step=1, weight_decay=float("inf"))), EINVAL),
   ("mode 6", step([T()], A.hparams(step=1, mode=6)), EINVAL),

@@ -262,6 +262,21 @@ def test_edge_cases(env):
                grad_scale=1e-37)
 
 
+def test_large_scales_and_eps(env):
+    """Block scales above 2^100, where the reciprocal of the scale takes the exact division
+    branch: |g| ~ 1e17 gives v' ~ 1e31 (2^103); with beta2 = 0, v' = g^2 reaches 2^127, so 1/s is
+    subnormal; and an eps of 2^60, near the top of its range (2^64).  Every step replayed."""
+    A = env[0]
+    sizes = [4096, 128 * 9 + 1, 200]
+    flags = [0, A.T_HEAD, 0]
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 1), (2, 1, 0, 1), (3, 0, 1, 0)],
+               seed=21, grad_scale=1e17)
+    _run_steps(env, sizes, flags, ["f32"] * 3, [(1, 0, -1, 0), (2, 1, 0, 1), (3, 0, 1, 1)],
+               seed=22, grad_scale=3e18, hp_extra=dict(beta2=0.0))
+    _run_steps(env, sizes, flags, ["bf16"] * 3, [(1, 0, -1, 1), (2, 1, 0, 0), (3, 5, 1, 0)],
+               seed=23, hp_extra=dict(eps=2.0 ** 60))
+
+
 def test_run_twice_bit_identical(env):
     """Same inputs, same step: identical bits (no race in the block reductions)."""
     import torch
