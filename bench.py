@@ -26,6 +26,10 @@ value more); --shard-of N times rank 0's share of an N-way 128-aligned split of 
 --optimizer adds an "optimizer" object: the torch front end's opt.step() on the list as a BF16
 model (GPU and host time).
 
+python bench.py --hbm-study [FILTER] runs the measurement program hbm_mix_probe (built by the
+package's build step): the step's byte mix over 2.7B values under many access patterns, one CSV
+line per pattern (see its source for the names).
+
 python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR [--workload W]
 reads rocprofv3 CSV output (kernel trace + stats, FETCH_SIZE pass, WRITE_SIZE pass, each from
 a run with --copy-calibration), prints a text summary and writes profiles/counters_<W>.json.
@@ -48,6 +52,7 @@ METRIC = "optimizer-step G params/s and achieved HBM GB/s (% of peak), 2.7B list
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "bit_adamw_step_amd", "csrc", "adamw4_kernels.hip")
 CEILING_LIB = os.path.join(ROOT, "bit_adamw_step_amd", "libadamw4_ceiling.so")
+PROBE_EXE = os.path.join(ROOT, "bit_adamw_step_amd", "hbm_mix_probe")
 STEP_KERNEL = "adamw4::step_kernel"
 CALIB_BYTES = 4 << 30          # the --copy-calibration copy: 4 GiB read + 4 GiB written
 
@@ -424,7 +429,16 @@ def main():
     ap.add_argument("--optimizer", action="store_true",
                     help="also time the torch front end end to end on the workload as a BF16 model")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
+    ap.add_argument("--hbm-study", nargs="?", const="", default=None, metavar="FILTER",
+                    help="run the byte-mix bandwidth probe (all patterns, or those matching FILTER)")
+    ap.add_argument("--hbm-reps", type=int, default=5)
     args = ap.parse_args()
+    if args.hbm_study is not None:
+        import subprocess
+        if not os.path.exists(PROBE_EXE):
+            sys.exit(f"{PROBE_EXE} is not built (run the package's build step)")
+        cmd = [PROBE_EXE] + ([args.hbm_study, str(args.hbm_reps)] if args.hbm_study else [])
+        sys.exit(subprocess.run(cmd).returncode)
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, args.workload)
         return

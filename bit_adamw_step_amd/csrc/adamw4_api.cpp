@@ -13,6 +13,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -25,7 +26,6 @@ using namespace adamw4;
 namespace {
 
 constexpr size_t kNoOffset = SIZE_MAX;
-constexpr int kMaxPlans = 8;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
@@ -157,19 +157,6 @@ TensorDesc make_desc(const adamw4_tensor& t, uint32_t pos) {
     return d;
 }
 
-// Device memory for one launch's descriptors and chunk table.
-struct Plan {
-    int device = -1;
-    int workgroups = 0;             // the launch grid the chunk table is dealt for
-    std::vector<TensorDesc> descs;  // host copy, also the cache key
-    uint32_t nchunks = 0;
-    uint32_t ntails = 0;
-    bool extra = false;             // some tensor has a BF16 copy or a shard offset
-    size_t tails_off = 0;           // byte offset of the tail list in dbuf
-    void* dbuf = nullptr;
-    uint64_t last_use = 0;
-};
-
 struct DeviceInfo {
     int cus = 0;
     int step_bpc[6] = {0, 0, 0, 0, 0, 0};   // per v rule (adamw4_mode)
@@ -177,7 +164,6 @@ struct DeviceInfo {
 };
 
 std::mutex g_mu;
-std::vector<Plan*> g_plans;
 uint64_t g_clock = 0;
 std::vector<DeviceInfo> g_dev;
 
@@ -197,7 +183,6 @@ adamw4_status device_info(int dev, DeviceInfo& out) {
     return ADAMW4_OK;
 }
 
-
 // Units (128-value blocks) a launch walks for tensor d.  Step plans (split_tails) leave the
 // partial last block of a quantized tensor to the tail list.
 uint64_t plan_units(const TensorDesc& d, bool split_tails) {
@@ -205,23 +190,22 @@ uint64_t plan_units(const TensorDesc& d, bool split_tails) {
     return uint64_t((d.numel + kBlock - 1) / kBlock);
 }
 
-
-
-// Build descriptor, chunk and tail tables and copy them to a fresh device buffer.
-adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int workgroups, bool split_tails,
-                         Plan*& out) {
+// The chunk table and the tail list of a launch, built on the host.  cu = 0 picks the chunk
+// size from the list's size and the grid.
+adamw4_status make_tables(const std::vector<TensorDesc>& descs, uint64_t workgroups, uint32_t cu,
+                          bool split_tails, std::vector<Chunk>& chunks, std::vector<uint32_t>& tails) {
     uint64_t total_units = 0;
     for (const TensorDesc& d : descs) {
         // chunk starts are 32-bit block indices (2^32 blocks = 2^39 values per tensor)
         if (plan_units(d, split_tails) > uint64_t(UINT32_MAX)) return ADAMW4_ESIZE;
         total_units += plan_units(d, split_tails);
     }
-    const uint32_t cu = pick_chunk_units(total_units, uint64_t(workgroups));
-    std::vector<Chunk> chunks;
-    std::vector<uint32_t> tails;
+    if (cu == 0) cu = pick_chunk_units(total_units, workgroups);
     uint64_t nch = 0;
     for (const TensorDesc& d : descs) nch += (plan_units(d, split_tails) + cu - 1) / cu;
     if (nch > UINT32_MAX) return ADAMW4_ESIZE;
+    chunks.clear();
+    tails.clear();
     chunks.reserve(size_t(nch));
     for (size_t i = 0; i < descs.size(); ++i) {
         const uint64_t units = plan_units(descs[i], split_tails);
@@ -230,79 +214,217 @@ adamw4_status build_plan(std::vector<TensorDesc>&& descs, int dev, int workgroup
         if (split_tails && (descs[i].flags & D_QUANT) && descs[i].numel % kBlock != 0)
             tails.push_back(uint32_t(i));
     }
-    balance_chunks(chunks, uint64_t(workgroups));
+    balance_chunks(chunks, workgroups);
     if (chunks.size() > UINT32_MAX) return ADAMW4_ESIZE;
-    const size_t dbytes = align16(descs.size() * sizeof(TensorDesc));
-    const size_t cbytes = align16(chunks.size() * sizeof(Chunk));
-    const size_t bytes = dbytes + cbytes + tails.size() * sizeof(uint32_t);
-    void* dbuf = nullptr;
-    if (hipMalloc(&dbuf, std::max<size_t>(bytes, 16)) != hipSuccess) return ADAMW4_ENOMEM;
-    std::vector<char> host(bytes);
-    std::memcpy(host.data(), descs.data(), descs.size() * sizeof(TensorDesc));
-    std::memcpy(host.data() + dbytes, chunks.data(), chunks.size() * sizeof(Chunk));
-    std::memcpy(host.data() + dbytes + cbytes, tails.data(), tails.size() * sizeof(uint32_t));
-    // a fresh buffer: a blocking copy orders it before any later use on any stream
-    if (hipMemcpy(dbuf, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipFree(dbuf);
-        return ADAMW4_EHIP;
-    }
-    Plan* p = new Plan;
-    p->device = dev;
-    p->workgroups = workgroups;
-    p->descs = std::move(descs);
-    p->nchunks = uint32_t(chunks.size());
-    p->ntails = uint32_t(tails.size());
-    for (const TensorDesc& d : p->descs) p->extra = p->extra || d.wcopy != nullptr || d.base != 0;
-    p->tails_off = dbytes + cbytes;
-    p->dbuf = dbuf;
-    out = p;
     return ADAMW4_OK;
 }
 
-void free_plan(Plan* p) {
+// The last launch of each stream that read a device table: before the table is rewritten or
+// freed, the host waits for these launches only (never for the whole device).
+struct Uses {
+    std::vector<std::pair<hipStream_t, hipEvent_t>> ev;
+
+    adamw4_status record(hipStream_t s) {
+        for (auto& e : ev)
+            if (e.first == s) return hipEventRecord(e.second, s) == hipSuccess ? ADAMW4_OK : ADAMW4_EHIP;
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return ADAMW4_EHIP;
+        ev.emplace_back(s, e);
+        return hipEventRecord(e, s) == hipSuccess ? ADAMW4_OK : ADAMW4_EHIP;
+    }
+    adamw4_status wait() const {
+        for (const auto& e : ev)
+            if (hipEventSynchronize(e.second) != hipSuccess) return ADAMW4_EHIP;
+        return ADAMW4_OK;
+    }
+    void release() {
+        for (auto& e : ev) (void)hipEventDestroy(e.second);
+        ev.clear();
+    }
+};
+
+// The launch shape of a step: chunk and tail tables in device memory.  They depend only on each
+// tensor's numel and on whether it is quantized (and on the grid and chunk size), so a training
+// loop builds one shape plan and keeps it however its buffers move.
+struct ShapePlan {
+    int device = -1;
+    int workgroups = 0;
+    uint32_t chunk_override = 0;
+    std::vector<uint64_t> key;      // per tensor: numel << 1 | quantized
+    uint32_t nchunks = 0;
+    uint32_t ntails = 0;
+    size_t tails_off = 0;           // byte offset of the tail list in dbuf
+    void* dbuf = nullptr;
+    Uses uses;
+    uint64_t last_use = 0;
+};
+
+// One descriptor table in device memory with its pinned staging copy.  A step whose descriptors
+// (pointers, sizes, flags, keys) equal a resident table's reuses it; otherwise the least
+// recently used slot of the device is refilled by an asynchronous copy on the caller's stream.
+struct DescSlot {
+    int device = -1;
+    void* dev = nullptr;
+    void* host = nullptr;           // pinned staging
+    size_t cap = 0;
+    std::vector<TensorDesc> content;
+    bool valid = false;
+    hipEvent_t uploaded = nullptr;  // after the copy into dev
+    hipStream_t upload_stream = nullptr;
+    Uses uses;
+    uint64_t last_use = 0;
+};
+
+constexpr int kMaxShapePlans = 8;
+constexpr int kDescSlotsPerDevice = 4;
+std::vector<ShapePlan*> g_shapes;
+std::vector<DescSlot*> g_slots;
+
+adamw4_status free_shape(ShapePlan* p) {
+    adamw4_status s = p->uses.wait();
+    p->uses.release();
     if (p->dbuf) (void)hipFree(p->dbuf);
     delete p;
+    return s;
 }
 
-Launch launch_of(const Plan& p, int grid_cap) {
-    Launch L;
-    L.descs = static_cast<const TensorDesc*>(p.dbuf);
-    L.chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(p.dbuf) +
-                                              align16(p.descs.size() * sizeof(TensorDesc)));
-    L.nchunks = p.nchunks;
-    L.grid = int(std::min<uint64_t>(p.nchunks, uint64_t(std::max(grid_cap, 1))));
-    L.tails = reinterpret_cast<const uint32_t*>(static_cast<const char*>(p.dbuf) + p.tails_off);
-    L.ntails = p.ntails;
-    L.extra = p.extra;
-    return L;
+std::vector<uint64_t> shape_key(const std::vector<TensorDesc>& descs) {
+    std::vector<uint64_t> k(descs.size());
+    for (size_t i = 0; i < descs.size(); ++i)
+        k[i] = (uint64_t(descs[i].numel) << 1) | ((descs[i].flags & D_QUANT) ? 1u : 0u);
+    return k;
 }
 
-// Find or create the cached plan for this descriptor list (the common case in training: the
-// same buffers every step, so the tables are uploaded once).  Evicting a plan waits for the
-// device so no in-flight launch still reads it.
-adamw4_status get_plan(std::vector<TensorDesc>&& descs, int dev, int workgroups, Plan*& out) {
-    for (Plan* p : g_plans) {
-        if (p->device == dev && p->workgroups == workgroups && p->descs.size() == descs.size() &&
-            std::memcmp(p->descs.data(), descs.data(), descs.size() * sizeof(TensorDesc)) == 0) {
+// Find or build the shape plan (built once per list shape: one allocation and a blocking
+// upload of the tables).  Evicting the least recently used of more than kMaxShapePlans plans
+// waits for that plan's own last launches.
+adamw4_status get_shape(const std::vector<TensorDesc>& descs, int dev, int workgroups,
+                        uint32_t chunk_override, ShapePlan*& out) {
+    std::vector<uint64_t> key = shape_key(descs);
+    for (ShapePlan* p : g_shapes) {
+        if (p->device == dev && p->workgroups == workgroups && p->chunk_override == chunk_override &&
+            p->key == key) {
             p->last_use = ++g_clock;
             out = p;
             return ADAMW4_OK;
         }
     }
-    Plan* p = nullptr;
-    adamw4_status s = build_plan(std::move(descs), dev, workgroups, true, p);
+    std::vector<Chunk> chunks;
+    std::vector<uint32_t> tails;
+    adamw4_status s = make_tables(descs, uint64_t(workgroups), chunk_override, true, chunks, tails);
     if (s != ADAMW4_OK) return s;
-    if (g_plans.size() >= size_t(kMaxPlans)) {
-        auto lru = std::min_element(g_plans.begin(), g_plans.end(),
-                                    [](const Plan* a, const Plan* b) { return a->last_use < b->last_use; });
-        (void)hipDeviceSynchronize();
-        free_plan(*lru);
-        g_plans.erase(lru);
+    if (g_shapes.size() >= size_t(kMaxShapePlans)) {
+        auto lru = std::min_element(g_shapes.begin(), g_shapes.end(), [](const ShapePlan* a, const ShapePlan* b) {
+            return a->last_use < b->last_use;
+        });
+        ShapePlan* victim = *lru;
+        g_shapes.erase(lru);
+        if ((s = free_shape(victim)) != ADAMW4_OK) return s;
     }
+    const size_t cbytes = align16(chunks.size() * sizeof(Chunk));
+    const size_t bytes = cbytes + tails.size() * sizeof(uint32_t);
+    void* dbuf = nullptr;
+    if (hipMalloc(&dbuf, std::max<size_t>(bytes, 16)) != hipSuccess) return ADAMW4_ENOMEM;
+    std::vector<char> host(bytes);
+    std::memcpy(host.data(), chunks.data(), chunks.size() * sizeof(Chunk));
+    std::memcpy(host.data() + cbytes, tails.data(), tails.size() * sizeof(uint32_t));
+    // a fresh buffer: a blocking copy orders it before any later use on any stream
+    if (bytes && hipMemcpy(dbuf, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dbuf);
+        return ADAMW4_EHIP;
+    }
+    ShapePlan* p = new ShapePlan;
+    p->device = dev;
+    p->workgroups = workgroups;
+    p->chunk_override = chunk_override;
+    p->key = std::move(key);
+    p->nchunks = uint32_t(chunks.size());
+    p->ntails = uint32_t(tails.size());
+    p->tails_off = cbytes;
+    p->dbuf = dbuf;
     p->last_use = ++g_clock;
-    g_plans.push_back(p);
+    g_shapes.push_back(p);
     out = p;
     return ADAMW4_OK;
+}
+
+// A device-resident descriptor table equal to descs, uploaded on `stream` if none is.  Only a
+// list larger than the slot has held before allocates (device buffer and pinned staging, grown
+// to at least twice the old size); refilling a slot waits for the launches that last read it.
+adamw4_status get_descs(const std::vector<TensorDesc>& descs, int dev, hipStream_t stream,
+                        DescSlot*& out) {
+    const size_t bytes = descs.size() * sizeof(TensorDesc);
+    DescSlot* lru = nullptr;
+    int on_dev = 0;
+    for (DescSlot* d : g_slots) {
+        if (d->device != dev) continue;
+        ++on_dev;
+        if (d->valid && d->content.size() == descs.size() &&
+            std::memcmp(d->content.data(), descs.data(), bytes) == 0) {
+            // resident: a launch on another stream waits for the upload on the device
+            if (d->upload_stream != stream && hipStreamWaitEvent(stream, d->uploaded, 0) != hipSuccess)
+                return ADAMW4_EHIP;
+            d->last_use = ++g_clock;
+            out = d;
+            return ADAMW4_OK;
+        }
+        if (!lru || d->last_use < lru->last_use) lru = d;
+    }
+    DescSlot* d = lru;
+    if (on_dev < kDescSlotsPerDevice) {
+        d = new DescSlot;
+        d->device = dev;
+        if (hipEventCreateWithFlags(&d->uploaded, hipEventDisableTiming) != hipSuccess) {
+            delete d;
+            return ADAMW4_EHIP;
+        }
+        g_slots.push_back(d);
+    } else {
+        // the slot's readers and its last upload (which read the staging copy) must be done
+        if (d->uses.wait() != ADAMW4_OK || hipEventSynchronize(d->uploaded) != hipSuccess)
+            return ADAMW4_EHIP;
+    }
+    d->valid = false;
+    if (d->cap < bytes) {
+        const size_t cap = std::max(bytes, 2 * d->cap);
+        if (d->dev) (void)hipFree(d->dev);
+        if (d->host) (void)hipHostFree(d->host);
+        d->dev = d->host = nullptr;
+        d->cap = 0;
+        if (hipMalloc(&d->dev, cap) != hipSuccess) return ADAMW4_ENOMEM;
+        if (hipHostMalloc(&d->host, cap, hipHostMallocDefault) != hipSuccess) {
+            (void)hipFree(d->dev);
+            d->dev = nullptr;
+            return ADAMW4_ENOMEM;
+        }
+        d->cap = cap;
+    }
+    std::memcpy(d->host, descs.data(), bytes);
+    if (hipMemcpyAsync(d->dev, d->host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+        hipEventRecord(d->uploaded, stream) != hipSuccess)
+        return ADAMW4_EHIP;
+    d->upload_stream = stream;
+    d->content = descs;
+    d->valid = true;
+    d->last_use = ++g_clock;
+    out = d;
+    return ADAMW4_OK;
+}
+
+// Test hooks: the step launch's workgroup count and chunk size (128-value blocks per chunk, a
+// power of two from 16 to 4096) can be forced through the environment; they change only how
+// the work is cut, never a result.  0 = the library's choice.
+int env_int(const char* name) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return 0;
+    char* end = nullptr;
+    const long x = std::strtol(v, &end, 10);
+    return (end && *end == 0 && x > 0 && x < (1L << 20)) ? int(x) : 0;
+}
+
+uint32_t chunk_override() {
+    const int c = env_int("ADAMW4_CHUNK_OVERRIDE");
+    return (c >= kPlanRows && c <= 4096 && (c & (c - 1)) == 0) ? uint32_t(c) : 0u;
 }
 
 adamw4_status current_device(int& dev) {
@@ -354,15 +476,29 @@ adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hpara
     if ((s = current_device(dev)) != ADAMW4_OK) return s;
     DeviceInfo di;
     if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
-    Plan* p = nullptr;
-    const int grid = di.cus * di.step_bpc[hp->mode];
-    if ((s = get_plan(std::move(descs), dev, grid, p)) != ADAMW4_OK) return s;
-    const Launch L = launch_of(*p, grid);
-    if (launch_step(L, a, static_cast<hipStream_t>(stream)) != hipSuccess) return ADAMW4_EHIP;
-    return ADAMW4_OK;
+    const int grid_env = env_int("ADAMW4_GRID_OVERRIDE");
+    const int grid = grid_env ? grid_env : di.cus * di.step_bpc[hp->mode];
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ShapePlan* sp = nullptr;
+    if ((s = get_shape(descs, dev, grid, chunk_override(), sp)) != ADAMW4_OK) return s;
+    DescSlot* ds = nullptr;
+    if ((s = get_descs(descs, dev, st, ds)) != ADAMW4_OK) return s;
+    Launch L;
+    L.descs = static_cast<const TensorDesc*>(ds->dev);
+    L.chunks = static_cast<const Chunk*>(sp->dbuf);
+    L.nchunks = sp->nchunks;
+    L.grid = int(std::min<uint64_t>(sp->nchunks, uint64_t(grid)));
+    L.tails = reinterpret_cast<const uint32_t*>(static_cast<const char*>(sp->dbuf) + sp->tails_off);
+    L.ntails = sp->ntails;
+    L.extra = false;
+    for (const TensorDesc& d : descs) L.extra = L.extra || d.wcopy != nullptr || d.base != 0;
+    if (launch_step(L, a, st) != hipSuccess) return ADAMW4_EHIP;
+    if ((s = sp->uses.record(st)) != ADAMW4_OK) return s;
+    return ds->uses.record(st);
 }
 
-// init and decode: a one-off plan, freed after the stream has finished with it.
+// init and decode: one-off tables in a temporary buffer, freed after the stream has finished
+// with them (these calls wait for their work).
 static adamw4_status run_aux(std::vector<TensorDesc>&& descs, bool init, int32_t mode,
                              void* stream) {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -371,13 +507,32 @@ static adamw4_status run_aux(std::vector<TensorDesc>&& descs, bool init, int32_t
     if ((s = current_device(dev)) != ADAMW4_OK) return s;
     DeviceInfo di;
     if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
-    Plan* p = nullptr;
-    if ((s = build_plan(std::move(descs), dev, di.cus * di.aux_bpc, false, p)) != ADAMW4_OK) return s;
-    const Launch L = launch_of(*p, di.cus * di.aux_bpc);
+    const int grid = di.cus * di.aux_bpc;
+    std::vector<Chunk> chunks;
+    std::vector<uint32_t> tails;
+    if ((s = make_tables(descs, uint64_t(grid), 0, false, chunks, tails)) != ADAMW4_OK) return s;
+    const size_t dbytes = align16(descs.size() * sizeof(TensorDesc));
+    const size_t bytes = dbytes + chunks.size() * sizeof(Chunk);
+    void* dbuf = nullptr;
+    if (hipMalloc(&dbuf, std::max<size_t>(bytes, 16)) != hipSuccess) return ADAMW4_ENOMEM;
+    std::vector<char> host(bytes);
+    std::memcpy(host.data(), descs.data(), descs.size() * sizeof(TensorDesc));
+    std::memcpy(host.data() + dbytes, chunks.data(), chunks.size() * sizeof(Chunk));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = init ? launch_init(L, mode, st) : launch_decode(L, mode, st);
-    hipError_t e2 = hipStreamSynchronize(st);
-    free_plan(p);
+    hipError_t e = hipMemcpy(dbuf, host.data(), bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess) {
+        Launch L;
+        L.descs = static_cast<const TensorDesc*>(dbuf);
+        L.chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(dbuf) + dbytes);
+        L.nchunks = uint32_t(chunks.size());
+        L.grid = int(std::min<uint64_t>(chunks.size(), uint64_t(grid)));
+        L.tails = nullptr;
+        L.ntails = 0;
+        L.extra = false;
+        e = init ? launch_init(L, mode, st) : launch_decode(L, mode, st);
+    }
+    const hipError_t e2 = hipStreamSynchronize(st);
+    (void)hipFree(dbuf);
     return (e == hipSuccess && e2 == hipSuccess) ? ADAMW4_OK : ADAMW4_EHIP;
 }
 
