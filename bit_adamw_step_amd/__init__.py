@@ -75,6 +75,8 @@ def lib():
         L.adamw4_init_state.restype = ctypes.c_int32
         L.adamw4_step.argtypes = [P, ctypes.c_int32, P, P]
         L.adamw4_step.restype = ctypes.c_int32
+        L.adamw4_step_noalloc.argtypes = [P, ctypes.c_int32, P, P]
+        L.adamw4_step_noalloc.restype = ctypes.c_int32
         L.adamw4_decode_state.argtypes = [P, ctypes.c_int32, P, P, P]
         L.adamw4_decode_state.restype = ctypes.c_int32
         L.adamw4_status_string.argtypes = [ctypes.c_int32]
@@ -134,6 +136,14 @@ def step(ts: ctypes.Array, hp: HParams, stream=None) -> None:
     """adamw4_step over a prepared tensor array."""
     _check(lib().adamw4_step(ctypes.addressof(ts) if len(ts) else None, len(ts), ctypes.byref(hp),
                              _stream_handle(stream)), "adamw4_step")
+
+
+def step_noalloc(ts: ctypes.Array, hp: HParams, stream=None) -> None:
+    """adamw4_step_noalloc: the same step with its tables in the library's fixed device array
+    (allocates nothing; calls on one GPU must not overlap)."""
+    _check(lib().adamw4_step_noalloc(ctypes.addressof(ts) if len(ts) else None, len(ts),
+                                     ctypes.byref(hp), _stream_handle(stream)),
+           "adamw4_step_noalloc")
 
 
 def init_state(ts: ctypes.Array, mode: int, m0=None, v0=None, stream=None) -> None:

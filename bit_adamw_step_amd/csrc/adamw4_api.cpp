@@ -454,21 +454,28 @@ adamw4_status adamw4_codebook(int32_t which, float out[16]) {
     return ADAMW4_OK;
 }
 
-adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
-                          void* stream) {
+// Argument checks and descriptors shared by the two step entry points.
+static adamw4_status prepare_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
+                                  int32_t max_tensors, std::vector<TensorDesc>& descs) {
     if (!hp || n < 0 || (n > 0 && !ts)) return ADAMW4_EINVAL;
-    if (n > ADAMW4_MAX_TENSORS) return ADAMW4_ESIZE;
+    if (n > max_tensors) return ADAMW4_ESIZE;
     adamw4_status s = check_hparams(*hp);
     if (s != ADAMW4_OK) return s;
     for (int32_t i = 0; i < n; ++i)
         if ((s = check_tensor_step(ts[i])) != ADAMW4_OK) return s;
-    if (n == 0) return ADAMW4_OK;
-
-    std::vector<TensorDesc> descs(static_cast<size_t>(n));
+    descs.resize(static_cast<size_t>(n));
     for (int32_t i = 0; i < n; ++i) {
         descs[i] = make_desc(ts[i], uint32_t(i));
         descs[i].wcopy = ts[i].param_bf16;
     }
+    return ADAMW4_OK;
+}
+
+adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
+                          void* stream) {
+    std::vector<TensorDesc> descs;
+    adamw4_status s = prepare_step(ts, n, hp, ADAMW4_MAX_TENSORS, descs);
+    if (s != ADAMW4_OK || n == 0) return s;
     const StepArgs a = step_args(*hp);
 
     std::lock_guard<std::mutex> lock(g_mu);
@@ -495,6 +502,81 @@ adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hpara
     if (launch_step(L, a, st) != hipSuccess) return ADAMW4_EHIP;
     if ((s = sp->uses.record(st)) != ADAMW4_OK) return s;
     return ds->uses.record(st);
+}
+
+// The allocation-free step: the same launch with its tables in the fixed device array.  Layout
+// of the array: descriptors | first[0..n] (prefix sums of chunks per tensor) | tail list |
+// chunk table, each part 256-byte aligned.  The first three are built on the host and travel in
+// kernel arguments; the chunk table is written by plan_kernel.  Chunks are taken in list order
+// (no re-cut of the last rounds), starting from the size adamw4_step would pick and doubling
+// until the table fits.
+adamw4_status adamw4_step_noalloc(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
+                                  void* stream) {
+    static_assert(ADAMW4_NOALLOC_SCRATCH_BYTES == kNoallocScratchBytes, "array size");
+    std::vector<TensorDesc> descs;
+    adamw4_status s = prepare_step(ts, n, hp, ADAMW4_NOALLOC_MAX_TENSORS, descs);
+    if (s != ADAMW4_OK || n == 0) return s;
+    const StepArgs a = step_args(*hp);
+    const auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    std::vector<uint64_t> units(descs.size());
+    uint64_t total = 0;
+    for (size_t i = 0; i < descs.size(); ++i) {
+        units[i] = plan_units(descs[i], true);
+        if (units[i] > uint64_t(UINT32_MAX)) return ADAMW4_ESIZE;
+        total += units[i];
+    }
+    const size_t off_first = al(descs.size() * sizeof(TensorDesc));
+    const size_t off_tails = off_first + al((descs.size() + 1) * sizeof(uint32_t));
+    const size_t off_chunks = off_tails + al(descs.size() * sizeof(uint32_t));
+
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if ((s = current_device(dev)) != ADAMW4_OK) return s;
+    DeviceInfo di;
+    if ((s = device_info(dev, di)) != ADAMW4_OK) return s;
+    const int grid = di.cus * di.step_bpc[hp->mode];
+    uint32_t cu = pick_chunk_units(total, uint64_t(grid));
+    uint64_t nchunks = 0;
+    for (;;) {
+        nchunks = 0;
+        for (uint64_t u : units) nchunks += (u + cu - 1) / cu;
+        if (off_chunks + nchunks * sizeof(Chunk) <= kNoallocScratchBytes) break;
+        if (cu >= 4096) return ADAMW4_ESIZE;
+        cu *= 2;
+    }
+    // host image of descriptors | first | tails
+    std::vector<uint32_t> image(off_chunks / 4, 0u);
+    char* img = reinterpret_cast<char*>(image.data());
+    std::memcpy(img, descs.data(), descs.size() * sizeof(TensorDesc));
+    uint32_t* first = reinterpret_cast<uint32_t*>(img + off_first);
+    uint32_t* tails = reinterpret_cast<uint32_t*>(img + off_tails);
+    uint32_t acc = 0, ntails = 0;
+    for (size_t i = 0; i < descs.size(); ++i) {
+        first[i] = acc;
+        acc += uint32_t((units[i] + cu - 1) / cu);
+        if ((descs[i].flags & D_QUANT) && descs[i].numel % kBlock != 0) tails[ntails++] = uint32_t(i);
+    }
+    first[descs.size()] = acc;
+    void* base = nullptr;
+    if (noalloc_scratch(&base) != hipSuccess) return ADAMW4_EHIP;
+    char* b = static_cast<char*>(base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (launch_upload(base, 0, image.data(), image.size(), st) != hipSuccess) return ADAMW4_EHIP;
+    const TensorDesc* d_descs = reinterpret_cast<const TensorDesc*>(b);
+    Chunk* d_chunks = reinterpret_cast<Chunk*>(b + off_chunks);
+    if (launch_plan(d_descs, reinterpret_cast<const uint32_t*>(b + off_first), uint32_t(descs.size()),
+                    cu, d_chunks, uint32_t(nchunks), st) != hipSuccess)
+        return ADAMW4_EHIP;
+    Launch L;
+    L.descs = d_descs;
+    L.chunks = d_chunks;
+    L.nchunks = uint32_t(nchunks);
+    L.grid = int(std::min<uint64_t>(nchunks, uint64_t(grid)));
+    L.tails = reinterpret_cast<const uint32_t*>(b + off_tails);
+    L.ntails = ntails;
+    L.extra = false;
+    for (const TensorDesc& d : descs) L.extra = L.extra || d.wcopy != nullptr || d.base != 0;
+    return launch_step(L, a, st) == hipSuccess ? ADAMW4_OK : ADAMW4_EHIP;
 }
 
 // init and decode: one-off tables in a temporary buffer, freed after the stream has finished

@@ -70,6 +70,18 @@ struct Launch {
 };
 
 hipError_t launch_step(const Launch& L, const StepArgs& a, hipStream_t s);
+
+// The allocation-free step's fixed device array (the current device's address, taken once per
+// device) and the kernels that fill it: upload copies host words carried in kernel arguments to
+// the array (at byte offset dst_off, a multiple of 4); plan writes the chunk table of a list
+// whose per-tensor chunk counts are prefix-summed in first[0..n] (first[n] = nchunks), chunks
+// of cu blocks in list order.
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** ptr);
+hipError_t launch_upload(void* scratch, size_t dst_off, const uint32_t* words, size_t nwords,
+                         hipStream_t s);
+hipError_t launch_plan(const TensorDesc* descs, const uint32_t* first, uint32_t ntensors,
+                       uint32_t cu, Chunk* chunks, uint32_t nchunks, hipStream_t s);
 hipError_t launch_init(const Launch& L, int32_t mode, hipStream_t s);
 hipError_t launch_decode(const Launch& L, int32_t mode, hipStream_t s);
 

@@ -186,6 +186,22 @@ adamw4_status adamw4_init_state(const adamw4_tensor* ts, int32_t n, int32_t mode
 adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
                           void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, allocation-free
+ * serving loops, harnesses that forbid hipMalloc): adamw4_step with the same arguments and
+ * bit-identical results that allocates nothing.  Its descriptor, chunk and tail tables live in
+ * one fixed device array of ADAMW4_NOALLOC_SCRATCH_BYTES bytes per GPU, which the library holds
+ * until the process ends; they are written by small kernels enqueued on `stream` (the host data
+ * travels in kernel arguments, so no host buffer outlives the call), and the call waits for
+ * nothing.  A list of more than ADAMW4_NOALLOC_MAX_TENSORS tensors, or one whose chunk table
+ * does not fit the array even at the largest chunk size, returns ADAMW4_ESIZE before anything is
+ * enqueued.  Every call on a GPU uses that GPU's one array and leaves its tables there: calls
+ * that overlap on one GPU (on different streams without ordering between them, or from several
+ * host threads at once) race and must not be made; calls ordered on one stream are safe. */
+#define ADAMW4_NOALLOC_SCRATCH_BYTES (4u << 20)
+#define ADAMW4_NOALLOC_MAX_TENSORS 4096
+adamw4_status adamw4_step_noalloc(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
+                                  void* stream);
+
 /* Decode one tensor's state into FP32 moments: the decode stage that opens each step in
  * [daiwk-PM]'s flowchart, m = NF4[code] s_m and v = V[code] s_v, written out (test and
  * checkpoint aid).  m_out, v_out are device arrays of t->numel floats, 16-B aligned (either

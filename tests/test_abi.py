@@ -137,6 +137,9 @@ def T(**kw):
 def step(ts, hp, n=None):
     arr = (A.Tensor * len(ts))(*ts)
     return L.adamw4_step(ctypes.addressof(arr) if ts else None, len(ts) if n is None else n, ctypes.byref(hp), None)
+def step_na(ts, hp):
+    arr = (A.Tensor * len(ts))(*ts)
+    return L.adamw4_step_noalloc(ctypes.addressof(arr), len(ts), ctypes.byref(hp), None)
 good = A.hparams(step=1)
 cases = [
   ("null hp", L.adamw4_step(None, 0, None, None), EINVAL),
@@ -180,6 +183,10 @@ cases = [
   ("layout null", L.adamw4_state_layout(100, 0, None), EINVAL),
   ("codebook 3", L.adamw4_codebook(3, None), EINVAL),
   ("empty list is a no-op", L.adamw4_step(None, 0, ctypes.byref(good), None), 0),
+  ("noalloc: empty list is a no-op", L.adamw4_step_noalloc(None, 0, ctypes.byref(good), None), 0),
+  ("noalloc: more tensors than its array holds", step_na([T()] * 4097, good), ESIZE),
+  ("noalloc: bad hparams", step_na([T()], A.hparams(step=0)), EINVAL),
+  ("noalloc: misaligned grad", step_na([T(grad=FAKE + 2)], good), EALIGN),
 ]
 bad = [(n, got, exp) for n, got, exp in cases if got != exp]
 print("RESULTS", len(cases), bad)

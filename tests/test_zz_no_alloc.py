@@ -1,0 +1,57 @@
+"""adamw4_step_noalloc, the entry point for callers that cannot allocate device memory, against
+adamw4_step on identical copies of a list: every weight, BF16 copy, code, scale and FP32 moment
+must be bit-identical.  Two lists in a row, the second smaller than the first (the fixed device
+array keeps the first call's tables), two steps each, through the C ABI."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_adamw_step_amd as A
+    return A
+
+
+def _make(A, sizes, flags, dts, copies, seed):
+    from gpu_harness import GpuList
+    gl = GpuList(sizes, flags, dts, seed=seed, copies=copies)
+    for st in gl.pl.states:        # alignment padding between state sections is never written
+        st.zero_()
+    gl.pl.init(A.ZIP_SR)
+    return gl
+
+
+def test_noalloc_equals_step(env):
+    import torch
+    from gpu_harness import say
+    A = env
+    lists = [
+        # ragged quantized tensors, the 4096 boundary, FP32-state tensors, an FP32-m tensor,
+        # a LM head, BF16 and FP32 gradients, one BF16 weight copy
+        ([128 * 3000 + 77, 4096, 300, 1 << 20, 128 * 17, 5000],
+         [A.T_HEAD, 0, 0, A.T_FP32_M, A.T_NORM, 0],
+         ["bf16", "f32", "bf16", "bf16", "f32", "bf16"],
+         [False, True, False, False, False, False]),
+        # smaller: fewer tensors, fewer chunks, one tail
+        ([4096 + 5, 200, 128 * 40], [0, A.T_NORM, A.T_HEAD], ["f32", "bf16", "bf16"],
+         [False, False, False]),
+    ]
+    for k, (sizes, flags, dts, copies) in enumerate(lists):
+        x = _make(A, sizes, flags, dts, copies, seed=60 + k)
+        y = _make(A, sizes, flags, dts, copies, seed=60 + k)
+        for t, mode, prev, srh in [(1, A.ZIP_SR, -1, 1), (2, A.ZE_EDEN, A.ZIP_SR, 0)]:
+            x.set_grads(t, seed=60 + k)
+            y.set_grads(t, seed=60 + k)
+            hp = A.hparams(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=8)
+            say(f"list {k} ({len(sizes)} tensors) step {t}: adamw4_step vs adamw4_step_noalloc")
+            A.step(x.pl.array, hp)
+            A.step_noalloc(y.pl.array, hp)
+            torch.cuda.synchronize()
+            outs_x = x.params + x.pl.states + [c for c in x.copies if c is not None]
+            outs_y = y.params + y.pl.states + [c for c in y.copies if c is not None]
+            for i, (a, b) in enumerate(zip(outs_x, outs_y)):
+                assert torch.equal(a, b), f"list {k} step {t}: output {i} differs"
