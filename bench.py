@@ -4,7 +4,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2b7] [--v-m
                 [--bf16-copy] [--shard-of N] [--optimizer] [--no-cpu-baseline] [--no-ceiling]
 
 One step = one adamw4_step call over the whole parameter list (every value: decode, AdamW,
-weight update, requantize, pack), inputs resident in HBM.  The default workload is the
+weight update, requantize, pack), inputs resident in HBM.  The K timed steps run back to back
+between two synchronisations (value, ms_per_step); the same K steps then run again with HIP
+events around each launch on the launch stream (per-launch median, percentiles, the roofline's
+achieved rate).  The default workload is the
 Llama-style 2.7B list (291 tensors, BF16 grads, ZIP-SR, LM-head m stochastically rounded in
 the last 10% of a 200-step schedule).  The K timed steps take t = 200/K, 2*200/K, ..., 200, so
 the stochastic-rounding phase has its share of the job.  Prints one JSON line.
@@ -30,9 +33,12 @@ python bench.py --hbm-study [FILTER] runs the measurement program hbm_mix_probe 
 package's build step): the step's byte mix over 2.7B values under many access patterns, one CSV
 line per pattern (see its source for the names).
 
-python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR [--workload W]
-reads rocprofv3 CSV output (kernel trace + stats, FETCH_SIZE pass, WRITE_SIZE pass, each from
-a run with --copy-calibration), prints a text summary and writes profiles/counters_<W>.json.
+python bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR [REQUEST_DIR] [--workload W]
+reads rocprofv3 CSV output (kernel trace + stats, FETCH_SIZE pass, WRITE_SIZE pass and, if given,
+a pass of read-request counts by size, each from a run with --copy-calibration), prints a text
+summary and writes profiles/counters_<W>.json.  With the request counts the read bytes are
+counted directly (128-, 64- and 32-byte requests times their sizes) and the copy-calibrated
+FETCH_SIZE is kept beside them as a cross-check.
 """
 from __future__ import annotations
 
@@ -159,15 +165,21 @@ def run_gpu(w, steps: int, warmup: int, device, v_mode: str | None = None, shard
     torch.cuda.synchronize()
     ts = timed_schedule(w, steps)
     hps = [hp(t) for t in ts]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ts]
+    # the timed job: K steps back to back, nothing else on the stream (timing events recorded
+    # between launches cost the GPU tens of microseconds each, which small lists would feel)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for h in hps:
+        pl.step(h, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the same K steps again with HIP events around each launch: per-launch times
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ts]
     for (a, b), h in zip(ev, hps):
         a.record(stream)
         pl.step(h, stream)
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in ev]   # ms per launch
     return pl, ts, per, wall
 
@@ -328,13 +340,15 @@ def cpu_baseline(w, pl, budget_s: float = 30.0):
 
 
 def traffic_from_profile(wname: str):
+    """(HBM bytes per launch, how they were counted) from the stored counters, or (None, None)
+    when there are none for the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"counters_{wname}.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     d = json.load(open(path))
     if d.get("kernel_sha") != kernel_hash():
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return None, None
+    return d.get("hbm_bytes_per_launch"), d.get("traffic_method")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -353,7 +367,23 @@ def _is_copy(name: str) -> bool:
     return "copyBuffer" in name or "copy" in name.lower() and "adamw4" not in name
 
 
-def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, wname: str) -> None:
+def _per_dispatch(d: str, counters) -> dict:
+    """{dispatch id: (kernel name, {counter: value summed over instances})}"""
+    per = {}
+    for r in _csv(d, "counter_collection.csv"):
+        if r["Counter_Name"] not in counters:
+            continue
+        nm, vals = per.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))
+        vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+REQ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                "TCC_EA0_RDREQ_128B_sum")
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, wname: str,
+                       req_dir: str | None = None) -> None:
     import workloads as W
     w = W.WORKLOADS[wname]
     bytes_alg, q, f = algorithmic_bytes(w)
@@ -401,8 +431,36 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, wname: st
               f"counted {cal_kib:.1f} KiB -> factor {factor:.4f}; "
               f"step {kib * 1024 * factor / 1e9:.3f} GB per launch")
     out["hbm_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    out["traffic_method"] = ("FETCH_SIZE x copy calibration + WRITE_SIZE x copy calibration "
+                             "(rocprofv3, per step dispatch)")
+    if req_dir:
+        per = _per_dispatch(req_dir, REQ_COUNTERS)
+        stepr = [v for nm, v in per.values() if STEP_KERNEL in nm]
+        copyr = [v for nm, v in per.values() if _is_copy(nm)]
+        def rbytes(v):
+            return (128 * v["TCC_EA0_RDREQ_128B_sum"] + 64 * v["TCC_EA0_RDREQ_64B_sum"] +
+                    32 * v["TCC_EA0_RDREQ_32B_sum"])
+        mean = lambda xs: sum(xs) / len(xs)
+        rb = mean([rbytes(v) for v in stepr])
+        unsized = mean([v["TCC_EA0_RDREQ_sum"] - v["TCC_EA0_RDREQ_32B_sum"] - v["TCC_EA0_RDREQ_64B_sum"]
+                        - v["TCC_EA0_RDREQ_128B_sum"] for v in stepr])
+        cal = max(rbytes(v) for v in copyr) if copyr else None
+        out["read_bytes_per_launch_from_requests"] = rb
+        out["read_requests_unsized_per_launch"] = unsized
+        out["calibration_copy_read_bytes_from_requests"] = cal
+        out["fetch_vs_requests"] = out["fetch_bytes_per_launch"] / rb
+        out["hbm_bytes_per_launch"] = rb + out["write_bytes_per_launch"]
+        out["traffic_method"] = ("read: TCC_EA0_RDREQ_128B*128 + RDREQ_64B*64 + RDREQ_32B*32; "
+                                 "write: WRITE_SIZE (64- and 32-byte write requests); the "
+                                 "copy-calibrated FETCH_SIZE agrees within "
+                                 f"{abs(out['fetch_vs_requests'] - 1) * 100:.2f}%")
+        print(f"\nread requests by size: step {len(stepr)} dispatches, {rb / 1e9:.3f} GB per launch "
+              f"({unsized:.0f} requests of no listed size); calibration copy "
+              f"{(cal or 0) / 1e9:.3f} GB of {CALIB_BYTES / 1e9:.3f} GB read; copy-calibrated "
+              f"FETCH_SIZE / request bytes = {out['fetch_vs_requests']:.5f}")
     print(f"\nHBM traffic per launch {out['hbm_bytes_per_launch'] / 1e9:.3f} GB vs algorithmic "
-          f"{bytes_alg / 1e9:.3f} GB (ratio {out['hbm_bytes_per_launch'] / bytes_alg:.4f})")
+          f"{bytes_alg / 1e9:.3f} GB (ratio {out['hbm_bytes_per_launch'] / bytes_alg:.4f}); "
+          f"{out['traffic_method']}")
     path = os.path.join(ROOT, "profiles", f"counters_{wname}.json")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     json.dump(out, open(path, "w"), indent=1)
@@ -428,7 +486,8 @@ def main():
                     help="time rank 0's share of an N-way 128-aligned split of every tensor")
     ap.add_argument("--optimizer", action="store_true",
                     help="also time the torch front end end to end on the workload as a BF16 model")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"))
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                    help="TRACE FETCH WRITE [REQUESTS] rocprofv3 output directories")
     ap.add_argument("--hbm-study", nargs="?", const="", default=None, metavar="FILTER",
                     help="run the byte-mix bandwidth probe (all patterns, or those matching FILTER)")
     ap.add_argument("--hbm-reps", type=int, default=5)
@@ -440,7 +499,10 @@ def main():
         cmd = [PROBE_EXE] + ([args.hbm_study, str(args.hbm_reps)] if args.hbm_study else [])
         sys.exit(subprocess.run(cmd).returncode)
     if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, args.workload)
+        dirs = args.summarize_profiles
+        if len(dirs) not in (3, 4):
+            ap.error("--summarize-profiles takes TRACE FETCH WRITE [REQUESTS]")
+        summarize_profiles(dirs[0], dirs[1], dirs[2], args.workload, dirs[3] if len(dirs) == 4 else None)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the 4-bit AdamW step needs no communication, a sharded "
@@ -468,6 +530,8 @@ def main():
         del a, b
         torch.cuda.empty_cache()
     bytes_alg, q, f = algorithmic_bytes(w, args.shard_of, args.bf16_copy)
+    traffic, traffic_method = (traffic_from_profile(w.name) if args.shard_of == 1 and
+                               not args.bf16_copy and not args.v_mode else (None, None))
     values = q + f
     ms = sum(per) / len(per)
     ms_wall = wall * 1000 / len(per)
@@ -507,8 +571,7 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profile(w.name) if args.shard_of == 1 and
-                     not args.bf16_copy and not args.v_mode else None},
+                     "traffic": traffic, "traffic_method": traffic_method},
         "ceiling": ceil,
         "cpu_baseline": None,
     }
