@@ -55,3 +55,42 @@ def test_noalloc_equals_step(env):
             outs_y = y.params + y.pl.states + [c for c in y.copies if c is not None]
             for i, (a, b) in enumerate(zip(outs_x, outs_y)):
                 assert torch.equal(a, b), f"list {k} step {t}: output {i} differs"
+
+
+@pytest.mark.timeout(900)
+def test_noalloc_equals_step_fullsize(env):
+    """The Llama-style 2.7B list (291 tensors, 2.7e9 values; its chunk table at 64-block chunks
+    would overflow the fixed array, so the allocation-free call takes 128-block chunks) stepped
+    by both entry points from identical copies: weights and every state byte equal, compared on
+    the device, over a round-to-nearest step and an LM-head stochastic-rounding step."""
+    import torch
+    import workloads as W
+    from gpu_harness import say
+    A = env
+    w = W.WORKLOADS["llama2b7"]
+    dev = torch.device("cuda:0")
+    lists = []
+    for copy in range(2):
+        params = [W.make_param(s, i, dev) for i, s in enumerate(w.specs)]
+        grads = [W.make_grad(w, s, i, 1, dev) for i, s in enumerate(w.specs)]
+        pl = A.ParamList(params, grads, [s.flags for s in w.specs])
+        for st in pl.states:
+            st.zero_()
+        pl.init(A.ZIP_SR)
+        lists.append(pl)
+    x, y = lists
+    for t, srh in [(1, 0), (2, 1)]:
+        if t > 1:
+            for i, s in enumerate(w.specs):
+                W.make_grad(w, s, i, t, dev, out=x.grads[i])
+                y.grads[i].copy_(x.grads[i])
+        hp = A.hparams(step=t, mode=A.ZIP_SR, sr_head=srh, seed=0)
+        say(f"2.7B list step {t}: adamw4_step vs adamw4_step_noalloc")
+        A.step(x.array, hp)
+        A.step_noalloc(y.array, hp)
+        torch.cuda.synchronize()
+        for i in range(len(w.specs)):
+            assert torch.equal(x.params[i].view(torch.int32), y.params[i].view(torch.int32)), (t, i)
+            assert torch.equal(x.states[i], y.states[i]), (t, i)
+    del lists, x, y
+    torch.cuda.empty_cache()
