@@ -196,7 +196,12 @@ adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hpara
  * does not fit the array even at the largest chunk size, returns ADAMW4_ESIZE before anything is
  * enqueued.  Every call on a GPU uses that GPU's one array and leaves its tables there: calls
  * that overlap on one GPU (on different streams without ordering between them, or from several
- * host threads at once) race and must not be made; calls ordered on one stream are safe. */
+ * host threads at once) race and must not be made; calls ordered on one stream are safe.
+ * Under stream capture the call records only kernel launches.  Their arguments, hp included,
+ * are fixed when recorded, so every replay of the graph repeats the same step t with the same
+ * seed on whatever the buffers then hold; a graph for step t+1 is a new capture.  Make one
+ * eager call on the GPU before its first capture: the first call on a device looks up the
+ * array's address and the device's properties. */
 #define ADAMW4_NOALLOC_SCRATCH_BYTES (4u << 20)
 #define ADAMW4_NOALLOC_MAX_TENSORS 4096
 adamw4_status adamw4_step_noalloc(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,

@@ -1,7 +1,10 @@
 """adamw4_step_noalloc, the entry point for callers that cannot allocate device memory, against
 adamw4_step on identical copies of a list: every weight, BF16 copy, code, scale and FP32 moment
 must be bit-identical.  Two lists in a row, the second smaller than the first (the fixed device
-array keeps the first call's tables), two steps each, through the C ABI."""
+array keeps the first call's tables), two steps each, through the C ABI.  Also the same call
+recorded into a HIP graph and replayed: after every replay the list equals an identical copy
+stepped by eager calls, with the program's own eager work and synchronizations between replays
+(a replay repeats the captured call exactly, hyperparameters and step number included)."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -94,3 +97,52 @@ def test_noalloc_equals_step_fullsize(env):
             assert torch.equal(x.states[i], y.states[i]), (t, i)
     del lists, x, y
     torch.cuda.empty_cache()
+
+
+def _outputs(gl):
+    return gl.params + gl.pl.states + [c for c in gl.copies if c is not None]
+
+
+def test_noalloc_graph_replays_equal_eager(env):
+    import torch
+    from gpu_harness import say
+    A = env
+    # ragged quantized tensors (a tail launch), an FP32-state tensor, an LM head, BF16 and FP32
+    # grads, one BF16 weight copy (the kernel instance with extras)
+    sizes = [128 * 700 + 33, 4096, 1000, 128 * 64, 5000]
+    flags = [A.T_HEAD, 0, A.T_NORM, 0, 0]
+    dts = ["bf16", "f32", "bf16", "bf16", "f32"]
+    copies = [False, False, False, True, False]
+    x = _make(A, sizes, flags, dts, copies, seed=90)     # stepped by the graph
+    y = _make(A, sizes, flags, dts, copies, seed=90)     # stepped eagerly
+    z = _make(A, [128 * 50, 700], [0, 0], ["bf16", "f32"], [False, False], seed=91)
+    for gl in (x, y, z):
+        gl.set_grads(1, seed=90)
+    hp = A.hparams(step=7, mode=A.ZIP_SR, sr_head=1, seed=4)
+    say("warm-up: one eager allocation-free step on both copies")
+    A.step_noalloc(x.pl.array, hp)
+    A.step_noalloc(y.pl.array, hp)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(_outputs(x), _outputs(y))):
+        assert torch.equal(a, b), f"warm-up: output {i} differs"
+
+    say("capture one adamw4_step_noalloc call into a graph")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.step_noalloc(x.pl.array, hp)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(_outputs(x), _outputs(y))):
+        assert torch.equal(a, b), f"capture changed output {i}"   # capture runs nothing
+
+    hz = A.hparams(step=3, mode=A.ZE_EDEN, prev_mode=A.ZIP_SR, seed=4)
+    for r in range(4):
+        say(f"replay {r}: graph on one copy, eager call on the other")
+        g.replay()
+        torch.cuda.synchronize()
+        A.step_noalloc(y.pl.array, hp)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(_outputs(x), _outputs(y))):
+            assert torch.equal(a, b), f"replay {r}: output {i} differs"
+        A.step(z.pl.array, hz)             # other work of the program between replays
+        torch.cuda.synchronize()
+    del g
