@@ -100,9 +100,11 @@ def test_no_writes_outside_buffers(env):
         assert gm.intact() and gv.intact()
 
 
-def test_shards_stay_inside_their_buffers(env):
+@pytest.mark.parametrize("entry", ["adamw4_step", "adamw4_step_noalloc"])
+def test_shards_stay_inside_their_buffers(env, entry):
     """Shard entries (offsets into their whole tensors, RNG keys, short shards kept quantized,
-    an FP32-m shard, ragged last blocks) between canaries: after four steps the canaries are
+    shards shorter than one block, which are all tail, an FP32-m shard, ragged last blocks)
+    between canaries, stepped through either entry point: after four steps the canaries are
     intact and every step matches the oracle's step of the same element range."""
     import torch
     from gpu_harness import oracle_state, compare_state, compare_weights, compare_bf16_copy, say, to_np
@@ -110,8 +112,9 @@ def test_shards_stay_inside_their_buffers(env):
     rng = np.random.default_rng(22)
     f32 = np.float32
     ents = [(300, A.T_SHARD, 1280), (128 * 5 + 7, A.T_SHARD | A.T_HEAD, 128 * 33),
-            (4095, A.T_SHARD, 0), (1000, A.T_SHARD | A.T_FP32_M, 256), (129, A.T_SHARD, 128 * 7)]
-    keys = [11, 12, 13, 14, 15]
+            (4095, A.T_SHARD, 0), (1000, A.T_SHARD | A.T_FP32_M, 256), (129, A.T_SHARD, 128 * 7),
+            (100, A.T_SHARD, 128 * 11), (1, A.T_SHARD | A.T_HEAD, 128 * 2)]
+    keys = [11, 12, 13, 14, 15, 16, 17]
     guards, params, grads, states, copies = [], [], [], [], []
     for n, f, off in ents:
         gp, gg, gc = Guarded(4 * n, rng), Guarded(2 * n, rng), Guarded(2 * n, rng)
@@ -142,8 +145,11 @@ def test_shards_stay_inside_their_buffers(env):
             g.copy_(torch.from_numpy(rng.normal(0, 1e-3, g.numel()).astype(f32)).to(g.dtype))
         kw = dict(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=4)
         gh = [to_np(g).copy() for g in grads]
-        say(f"guarded shard step t={t} mode={mode}")
-        pl.step(A.hparams(**kw))
+        say(f"guarded shard step t={t} mode={mode} through {entry}")
+        if entry == "adamw4_step":
+            pl.step(A.hparams(**kw))
+        else:
+            A.step_noalloc(pl.array, A.hparams(**kw))
         assert all(gd.intact() for gd in guards), f"canary overwritten at step {t}"
         rep = {}
         for i, (n, f, off) in enumerate(ents):

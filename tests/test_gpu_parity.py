@@ -277,6 +277,35 @@ def test_large_scales_and_eps(env):
                seed=23, hp_extra=dict(eps=2.0 ** 60))
 
 
+def test_extreme_hyperparameters(env):
+    """Hyperparameters at the edges of their ranges, every step replayed:
+    - the last step numbers the RNG counter holds (t = 2^32 - 2, 2^32 - 1, where both bias
+      corrections round to 1) with the largest seed;
+    - beta1 = 0 (m' = g), beta2 = 0.5, no weight decay;
+    - lr = 0: the weights keep their bits while the moments move;
+    - lr = 2e-3 at t = 1..3, where the update is as large as the N(0, 0.02) weights, so about
+      half of them cancel towards zero or change sign (the weight bar at its hardest);
+    - beta2 = 1 - 2^-24, the largest below 1, where bias correction divides by 1 - beta2^t ~ t 2^-24."""
+    A = env[0]
+    sizes = [4096, 128 * 9 + 1, 200, 128 * 64]
+    flags = [0, A.T_HEAD, 0, 0]
+    gdt = ["f32", "bf16", "f32", "bf16"]
+    top = (1 << 32) - 1
+    rep = {}
+    _run_steps(env, sizes, flags, gdt, [(top - 1, 0, -1, 1), (top, 1, 0, 1)], seed=31,
+               hp_extra=dict(seed=(1 << 64) - 1), report=rep)
+    _run_steps(env, sizes, flags, gdt, [(1, 0, -1, 1), (2, 0, -1, 0), (3, 1, 0, 1)], seed=32,
+               hp_extra=dict(beta1=0.0, beta2=0.5, weight_decay=0.0), report=rep)
+    _run_steps(env, sizes, flags, gdt, [(1, 0, -1, 1), (2, 1, 0, 0)], seed=33,
+               hp_extra=dict(lr=0.0), report=rep)
+    _run_steps(env, sizes, flags, gdt, [(1, 0, -1, 0), (2, 0, -1, 1), (3, 1, 0, 0)], seed=34,
+               hp_extra=dict(lr=2e-3), report=rep)
+    _run_steps(env, sizes, flags, gdt, [(1, 0, -1, 1), (2, 1, 0, 0), (3, 0, 1, 1)], seed=35,
+               hp_extra=dict(beta2=float(np.float32(1.0 - 2.0 ** -24))), report=rep)
+    exact = [v for k, v in rep.items() if k.endswith("w_bitexact")]
+    print(f"weights bit-exact in {sum(exact)} of {len(exact)} tensor-steps")
+
+
 def test_run_twice_bit_identical(env):
     """Same inputs, same step: identical bits (no race in the block reductions)."""
     import torch

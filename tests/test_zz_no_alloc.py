@@ -146,3 +146,34 @@ def test_noalloc_graph_replays_equal_eager(env):
         A.step(z.pl.array, hz)             # other work of the program between replays
         torch.cuda.synchronize()
     del g
+
+
+def test_noalloc_at_the_tensor_limit(env):
+    """The longest list the allocation-free call takes (4096 entries, ADAMW4_NOALLOC_MAX_TENSORS:
+    a hundred-odd upload launches, the plan kernel's search over every entry): FP32-state
+    tensors, quantized shards shorter than a block (all tail) and of a few blocks, a quantized
+    tensor of several chunks and an LM head, BF16 and FP32 grads.  Bit-identical to adamw4_step
+    over two steps."""
+    import numpy as np
+    import torch
+    from gpu_harness import say
+    A = env
+    n_max = 4096
+    rng = np.random.default_rng(70)
+    sizes = [int(x) for x in rng.integers(1, 1500, n_max)]
+    flags = [A.T_SHARD if k % 3 == 0 else 0 for k in range(n_max)]
+    sizes[5], flags[5] = 128 * 300 + 9, 0
+    sizes[4000], flags[4000] = 128 * 1000, A.T_HEAD
+    dts = ["bf16" if k % 2 else "f32" for k in range(n_max)]
+    x = _make(A, sizes, flags, dts, None, seed=70)
+    y = _make(A, sizes, flags, dts, None, seed=70)
+    for t, mode, prev, srh in [(1, A.ZIP_SR, -1, 1), (2, A.ZE_EDEN, A.ZIP_SR, 0)]:
+        x.set_grads(t, seed=70)
+        y.set_grads(t, seed=70)
+        hp = A.hparams(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=3)
+        say(f"{n_max} tensors, step {t}: adamw4_step vs adamw4_step_noalloc")
+        A.step(x.pl.array, hp)
+        A.step_noalloc(y.pl.array, hp)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(_outputs(x), _outputs(y))):
+            assert torch.equal(a, b), f"step {t}: output {i} differs"
