@@ -177,6 +177,7 @@ cases = [
   ("state too small", step([T(state_size=A.state_bytes(8192, 0) - 1)], good), ESIZE),
   ("fallback state too small", step([T(numel=100, state_size=799)], good), ESIZE),
   ("second tensor bad", step([T(), T(numel=-1)], good), EINVAL),
+  ("more tensors than a list holds", step([T()] * 65537, good), ESIZE),
   ("init bad mode", L.adamw4_init_state(None, 0, 7, None, None, None), EINVAL),
   ("decode null", L.adamw4_decode_state(None, 0, None, None, None), EINVAL),
   ("decode bad mode", L.adamw4_decode_state(ctypes.byref(T()), 6, None, None, None), EINVAL),

@@ -177,3 +177,63 @@ def test_launch_shape_does_not_change_bits(env, grid, chunk):
         del os.environ["ADAMW4_CHUNK_OVERRIDE"]
     for a, b in zip(base, other):
         assert torch.equal(a, b)
+
+
+def test_the_longest_list(env):
+    """adamw4_step at its tensor limit, 65536 entries (ADAMW4_MAX_TENSORS): FP32-state tensors,
+    quantized shards shorter than a block and of a few blocks, a quantized tensor of several
+    chunks and an LM head, BF16 grads; every tensor a view into shared buffers, each starting
+    16-byte aligned, with sentinel padding between the weight views.  One ZIP-SR step with the
+    LM head's stochastic rounding: 600-odd sampled tensors replayed on the oracle, and every
+    padding word still holds its sentinel."""
+    import torch
+    from gpu_harness import oracle_state, compare_state, compare_weights, to_np, say
+    A, orc = env
+    n_max = 65536
+    rng = np.random.default_rng(90)
+    sizes = [int(x) for x in rng.integers(1, 300, n_max)]
+    flags = [A.T_SHARD if k % 3 == 0 else 0 for k in range(n_max)]
+    sizes[7], flags[7] = 128 * 400 + 5, 0
+    sizes[n_max - 2], flags[n_max - 2] = 128 * 90, A.T_HEAD
+    pad8 = [(n + 7) // 8 * 8 for n in sizes]        # 16-byte starts for FP32 and BF16 views
+    offs = np.concatenate([[0], np.cumsum(pad8)]).astype(np.int64)
+    sb = [A.state_bytes(n, f) for n, f in zip(sizes, flags)]
+    soffs = np.concatenate([[0], np.cumsum(sb)]).astype(np.int64)
+    sentinel = 1234.5
+    total = int(offs[-1])
+    pad_np = np.ones(total, bool)
+    for k, n in enumerate(sizes):
+        pad_np[offs[k]: offs[k] + n] = False
+    pad = torch.from_numpy(pad_np).cuda()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(90)
+    wbuf = (torch.randn(total, generator=g) * 0.02).cuda()
+    wbuf[pad] = sentinel
+    gbuf = (torch.randn(total, generator=g) * 1e-3).to(torch.bfloat16).cuda()
+    sbuf = torch.zeros(int(soffs[-1]), dtype=torch.uint8, device="cuda")
+    params = [wbuf.narrow(0, int(offs[k]), n) for k, n in enumerate(sizes)]
+    grads = [gbuf.narrow(0, int(offs[k]), n) for k, n in enumerate(sizes)]
+    states = [sbuf.narrow(0, int(soffs[k]), sb[k]) for k in range(n_max)]
+    pl = A.ParamList(params, grads, flags, states=states)
+    say(f"init of {n_max} tensors")
+    pl.init(A.ZIP_SR)
+    torch.cuda.synchronize()
+    sample = sorted(set(range(0, n_max, 109)) | {7, n_max - 2, n_max - 1})
+    w0 = {i: to_np(params[i]).copy() for i in sample}
+    g0 = {i: to_np(grads[i]).copy() for i in sample}
+    s0 = {i: oracle_state(to_np(states[i]), sizes[i], flags[i]) for i in sample}
+    kw = dict(step=9, mode=A.ZIP_SR, sr_head=1, seed=12)
+    say(f"step of {n_max} tensors")
+    pl.step(A.hparams(**kw))
+    torch.cuda.synchronize()
+    assert torch.all(wbuf[pad] == sentinel), "a weight outside its view was written"
+    rep = {}
+    for i in sample:
+        n, f = sizes[i], flags[i]
+        w = w0[i]
+        dbg = orc.step_tensor(w, g0[i], s0[i], orc.HParams(**kw), pos=i, head=bool(f & A.T_HEAD),
+                              dbg=True)
+        compare_weights(f"{i}", to_np(params[i]), w, rep)
+        compare_state(f"{i}", n, oracle_state(to_np(states[i]), n, f), s0[i], dbg, rep)
+    exact = [v for k, v in rep.items() if k.endswith("w_bitexact")]
+    say(f"{len(sample)} sampled tensors match; weights bit-exact in {sum(exact)} of {len(exact)}")
