@@ -471,20 +471,26 @@ static adamw4_status prepare_step(const adamw4_tensor* ts, int32_t n, const adam
     return ADAMW4_OK;
 }
 
-// Workgroups for a step launch: the v rule's resident count per CU (step_blocks_per_cu), at
-// most 4 when most quantized values keep m in FP32.  Those move 19 B per value instead of
-// 12.125 B with the same arithmetic and stream faster with fewer waves: on the 834M list with
-// FP32 m, ZIP-SR and state-space SR ran 2.4% faster at 4 workgroups per CU than at 5.
+// Workgroups for a step launch: the v rule's count per CU for the plain byte mix
+// (step_blocks_per_cu), lowered for lists whose quantized values mostly move more bytes with
+// the same arithmetic, which stream faster with fewer waves:
+//  - with a BF16 weight copy (14.125 B per value instead of 12.125), one workgroup per CU
+//    fewer: 1.3-2.4% faster for every v rule on the 2.7B list;
+//  - with m in FP32 (19.06 B per value), two fewer: on the 834M study list ZIP-SR and
+//    state-space SR ran 4.4-4.6% faster at 3 than at 5, the round-to-nearest rules 2.4-3.3%
+//    faster at 2 than at 4.
 static int step_grid(const DeviceInfo& di, int32_t mode, const std::vector<TensorDesc>& descs) {
     int bpc = di.step_bpc[mode];
-    uint64_t quant = 0, fp32m = 0;
+    uint64_t quant = 0, fp32m = 0, copy = 0;
     for (const TensorDesc& d : descs) {
         if (!(d.flags & D_QUANT)) continue;
         quant += uint64_t(d.numel);
         if (d.flags & D_FP32M) fp32m += uint64_t(d.numel);
+        else if (d.wcopy) copy += uint64_t(d.numel);
     }
-    if (2 * fp32m > quant) bpc = std::min(bpc, 4);
-    return di.cus * bpc;
+    if (2 * fp32m > quant) bpc -= 2;
+    else if (2 * (fp32m + copy) > quant) bpc -= 1;
+    return di.cus * std::max(bpc, 1);
 }
 
 adamw4_status adamw4_step(const adamw4_tensor* ts, int32_t n, const adamw4_hparams* hp,
