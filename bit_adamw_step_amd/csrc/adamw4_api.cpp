@@ -471,25 +471,29 @@ static adamw4_status prepare_step(const adamw4_tensor* ts, int32_t n, const adam
     return ADAMW4_OK;
 }
 
-// Workgroups for a step launch: the v rule's count per CU for the plain byte mix
-// (step_blocks_per_cu), lowered for lists whose quantized values mostly move more bytes with
-// the same arithmetic, which stream faster with fewer waves:
-//  - with a BF16 weight copy (14.125 B per value instead of 12.125), one workgroup per CU
-//    fewer: 1.3-2.4% faster for every v rule on the 2.7B list;
-//  - with m in FP32 (19.06 B per value), two fewer: on the 834M study list ZIP-SR and
-//    state-space SR ran 4.4-4.6% faster at 3 than at 5, the round-to-nearest rules 2.4-3.3%
-//    faster at 2 than at 4.
+// Workgroups for a step launch: the v rule's count per CU for the plain byte mix of 12.125 B
+// per quantized value (step_blocks_per_cu), lowered when the list's quantized values move more
+// bytes with the same arithmetic, which streams faster with fewer waves.  Extra bytes per
+// value: 2 for FP32 grads (read), 2 for a BF16 weight copy (written), 6.94 for an FP32 m (read
+// and written instead of its codes and scales).  Averaged over the list's quantized values, 1 B
+// or more takes one workgroup per CU fewer and 5 B or more two fewer.  Measured, each against
+// the rule's plain count: FP32 grads (the stress list) 2.1-3.1% faster one lower; BF16 copies
+// (the 2.7B list) 1.3-2.4% faster one lower and slower two lower; FP32 m (the 834M study list)
+// 4.4-4.6% faster for ZIP-SR and state-space SR at 3 than at 5, 2.4-3.3% for the
+// round-to-nearest rules at 2 than at 4.
 static int step_grid(const DeviceInfo& di, int32_t mode, const std::vector<TensorDesc>& descs) {
-    int bpc = di.step_bpc[mode];
-    uint64_t quant = 0, fp32m = 0, copy = 0;
+    uint64_t quant = 0, extra16 = 0;   // extra bytes in sixteenths
     for (const TensorDesc& d : descs) {
         if (!(d.flags & D_QUANT)) continue;
-        quant += uint64_t(d.numel);
-        if (d.flags & D_FP32M) fp32m += uint64_t(d.numel);
-        else if (d.wcopy) copy += uint64_t(d.numel);
+        const uint64_t n = uint64_t(d.numel);
+        quant += n;
+        if (!(d.flags & D_BF16)) extra16 += 32 * n;
+        if (d.wcopy) extra16 += 32 * n;
+        if (d.flags & D_FP32M) extra16 += 111 * n;
     }
-    if (2 * fp32m > quant) bpc -= 2;
-    else if (2 * (fp32m + copy) > quant) bpc -= 1;
+    int bpc = di.step_bpc[mode];
+    if (quant > 0 && extra16 >= 80 * quant) bpc -= 2;
+    else if (quant > 0 && extra16 >= 16 * quant) bpc -= 1;
     return di.cus * std::max(bpc, 1);
 }
 
