@@ -67,11 +67,26 @@ MUTANTS = {
                         "        if (mode == ORC_ZE_EDEN) encode_v_eden_block(vw, V0, cv, &vscale[b]);"),
     "init_baseline_on_v0": ("        else encode_v_rtn_block(vw, uses_v1(mode) ? V1 : V0, cv, &vscale[b]);",
                             "        else encode_v_rtn_block(vw, V0, cv, &vscale[b]);"),
+    "v_beta_swapped": ("float v1 = hp->beta2 * v;", "float v1 = s->omb2 * v;"),
+    "zip_h_without_bias_correction": (
+        "                               uint8_t* codes, float* scale, orc_dbg* dbg) {\n    float s = 0.0f;\n"
+        "    for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);\n    *scale = s;\n    float c = sqrtf(s) * rs2;",
+        "                               uint8_t* codes, float* scale, orc_dbg* dbg) {\n    float s = 0.0f;\n"
+        "    for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);\n    *scale = s;\n    float c = sqrtf(s);"),
+    "prtn_h_without_bias_correction": (
+        "                                float eps, uint8_t* codes, float* scale, orc_dbg* dbg) {\n    float s = 0.0f;\n"
+        "    for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);\n    *scale = s;\n    float c = sqrtf(s) * rs2;",
+        "                                float eps, uint8_t* codes, float* scale, orc_dbg* dbg) {\n    float s = 0.0f;\n"
+        "    for (int j = 0; j < ORC_BLOCK; ++j) s = fmaxf(s, x[j]);\n    *scale = s;\n    float c = sqrtf(s);"),
+    "zip_eps_only_in_denominator": ("    n3 = n3 + eps;", "    n3 = n3 + 0.0f;"),
     "init_m_stochastic": ("        encode_m_block(mw, nvalid, 0, NF4, 0, 0, 0, 0, cm, &mscale[b], NULL);",
                           "        encode_m_block(mw, nvalid, 1, NF4, 0, 0, 0, 0, cm, &mscale[b], NULL);"),
 }
 
 PY_MUTANTS = {
+    "fallback_boundary_4095": ("MIN_QUANT = 4096", "MIN_QUANT = 4095"),
+    "fallback_boundary_4097": ("MIN_QUANT = 4096", "MIN_QUANT = 4097"),
+    "norm_layers_quantized": ("    return numel >= MIN_QUANT and not norm", "    return numel >= MIN_QUANT"),
     "init_fp32m_drops_m0": ("        m = np.zeros(n, np.float32) if m0 is None else np.asarray(m0, np.float32).copy()\n"
                             "        return State(True, None, full.vcodes",
                             "        m = np.zeros(n, np.float32)\n"

@@ -767,6 +767,24 @@ def test_state_bytes_match_pages(orc):
     assert round(G["bytes_per_param_fp32"] / G["bytes_per_param_4bit"], 2) == G["reduction_about"]
 
 
+def test_fallback_boundary(orc):
+    """Tensors below the pages' 4096-element boundary keep FP32 moments, 4096 and above are
+    quantized, and a normalization layer keeps FP32 moments at any size ([daiwk-LR] results
+    table and the line after it, [lav-ST])."""
+    G = json.load(open(os.path.join(GOLDEN, "a100_state_bytes.json")))
+    edge = G["fallback_below_elements"]
+    for n in (1, 255, edge - 1):
+        st = orc.init_state(n, False, orc.ZIP_SR)
+        assert not st.quantized and st.m.nbytes + st.v.nbytes == G["bytes_per_param_fp32"] * n, n
+    for n in (edge, edge + 1, 5 * edge):
+        st = orc.init_state(n, False, orc.ZIP_SR)
+        assert st.quantized, n
+        nbytes = st.mcodes.nbytes + st.vcodes.nbytes + st.mscale.nbytes + st.vscale.nbytes
+        assert nbytes == 2 * ((n + 1) // 2) + 2 * 4 * ((n + 127) // 128), n
+    st = orc.init_state(5 * edge, True, orc.ZIP_SR)
+    assert not st.quantized
+
+
 # ---------------------------------------------------------------------------------------------
 # P-14  determinism: thread count, sub-range replay
 # ---------------------------------------------------------------------------------------------
