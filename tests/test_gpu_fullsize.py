@@ -218,3 +218,66 @@ def test_llama2b7_rank0_share_equals_whole(env):
                 a = share.states[i][osh[k]:osh[k] + length]
                 b = whole.states[i][ow[k]:ow[k] + length]
                 assert torch.equal(a, b), (t, i, "state section", k)
+
+
+class _Spec:
+    def __init__(self, numel, flags):
+        self.numel, self.flags = numel, flags
+
+
+class _List:
+    def __init__(self, specs):
+        self.specs = specs
+
+
+@pytest.mark.timeout(900)
+def test_tensor_past_2_31_elements(env):
+    """One LM-head tensor of 2^31 + 717 values (element offsets, RNG counters and block indices
+    past 32-bit signed range; a ragged last block of 77 values) beside a small tensor, three
+    steps (ZIP-SR with the LM head's stochastic rounding, ZE-EDEN, ZIP-SR again), each replayed
+    on the oracle over sampled blocks: the first, those around element 2^31, the last full one,
+    the partial last one and 40 random ones."""
+    import torch
+    from gpu_harness import compare_state, compare_weights, say
+    A, orc = env
+    n_big = (1 << 31) + 128 * 5 + 77
+    lst = _List([_Spec(n_big, A.T_HEAD), _Spec(5000, 0)])
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    params = [torch.randn(s.numel, generator=gen, device=dev).mul_(0.02) for s in lst.specs]
+    grads = [torch.empty(s.numel, dtype=torch.bfloat16, device=dev) for s in lst.specs]
+    pl = A.ParamList(params, grads, [s.flags for s in lst.specs])
+    for st in pl.states:
+        st.zero_()
+    pl.init(A.ZIP_SR)
+    nb = (n_big + 127) // 128
+    rng = np.random.default_rng(31)
+    picks = {0, (1 << 24) - 2, (1 << 24) - 1, 1 << 24, (1 << 24) + 1, nb - 2, nb - 1}
+    picks |= set(rng.integers(0, nb, 40).tolist())
+    samples = [(0, 128 * b, min(128, n_big - 128 * b)) for b in sorted(picks)] + [(1, 0, 5000)]
+    report = {}
+    prev = A.ZIP_SR
+    for t, mode, srh in [(1, A.ZIP_SR, 1), (2, A.ZE_EDEN, 0), (3, A.ZIP_SR, 1)]:
+        for g in grads:
+            g.copy_(torch.randn(g.numel(), generator=gen, device=dev).mul_(1e-3))
+        kw = dict(step=t, mode=mode, prev_mode=prev, sr_head=srh, seed=5)
+        prev = mode
+        torch.cuda.synchronize()
+        before = [(i, e0, cnt) + _grab(pl, A, lst, i, e0, cnt) for (i, e0, cnt) in samples]
+        say(f"tensor of {n_big} values: step t={t} mode={mode} ({len(samples)} samples)")
+        pl.step(A.hparams(**kw))
+        torch.cuda.synchronize()
+        for (i, e0, cnt, wv, gv, st) in before:
+            s = lst.specs[i]
+            dbg = orc.step_tensor(wv, gv, st, orc.HParams(**kw), pos=i, head=bool(s.flags & A.T_HEAD),
+                                  e0=e0, n=s.numel, dbg=True)
+            w_now, _, st_now = _grab(pl, A, lst, i, e0, cnt)
+            name = f"big:t{t}:{i}@{e0}"
+            compare_weights(name, w_now, wv, report)
+            compare_state(name, cnt, st_now, st, dbg, report)
+    flips = sum(v for k, v in report.items() if k.endswith("_flips"))
+    exact = all(v for k, v in report.items() if k.endswith("_bitexact"))
+    say(f"  permitted stochastic flips {flips}, weights/FP32 states bit-exact {exact}")
+    del pl, params, grads
+    torch.cuda.empty_cache()
